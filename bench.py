@@ -1,0 +1,296 @@
+"""Benchmark of libtilepipe on one MI355X.
+
+One step = one pass of the pipelined map (scale-by-2) over 2**28 float32
+(1 GiB read, 1 GiB written), inputs resident in HBM. Prints ONE JSON line with
+the achieved HBM bandwidth, its fraction of the MI355X peak, the roofline of
+the dominant kernel, the CPU oracle's throughput on the same workload, and the
+other rows of the hot path (stage/tile sweep with the misaligned fallback, the
+predicated chunk copy, the compute-heavy map at 1/2/4 stages, the small
+double-buffered map, the row exchange).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--stages S] [--tile T]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+FP32_VALU_PEAK_TFLOPS = 78.6   # unpacked v_fma_f32: 256 CU x 128 lanes x 2 FLOP x 2.4 GHz
+METRIC = "achieved HBM GB/s (read+write) and % of MI355X peak, pipelined map, 1 GPU"
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--stages", type=int, default=3)
+    ap.add_argument("--tile", type=int, default=4096)
+    ap.add_argument("--tiles-per-block", type=int, default=64)
+    ap.add_argument("--quick", action="store_true", help="headline only: no sweep, no extra rows")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time of the oracle baseline")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ timing
+def time_launches(fn, warmup: int, steps: int):
+    """Run fn warmup times, then `steps` times between events on the current
+    stream (the one the library launches on). Returns (per-launch ms list,
+    whole-region ms)."""
+    import torch
+    s = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    r0 = torch.cuda.Event(enable_timing=True)
+    r1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    r0.record(s)
+    for i in range(steps):
+        starts[i].record(s)
+        fn()
+        ends[i].record(s)
+    r1.record(s)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    return per, r0.elapsed_time(r1)
+
+
+def median(v):
+    v = sorted(v)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+
+def kernel_source_hash() -> str:
+    """Hash of the kernel sources: a stored hardware-counter reading is only
+    reported while it still describes the kernels being run."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "software_pipelining_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(key: str):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = d.get(key)
+    if not e or e.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+# -------------------------------------------------------------- workloads
+def sampled_parity(x_host, y_dev, op, windows=16, width=4096, seed=0):
+    """Compare random windows of the GPU output with the oracle on the same
+    host input (bitwise)."""
+    import numpy as np
+    import oracle
+    n = x_host.numel()
+    rng = np.random.default_rng(seed)
+    xs = x_host.numpy()
+    for lo in rng.integers(0, max(1, n - width), size=windows):
+        hi = min(n, int(lo) + width)
+        exp = oracle.pipelined_map(xs[lo:hi], op, threads=1)
+        got = y_dev[lo:hi].cpu().numpy()
+        if not np.array_equal(got.view(np.uint32), exp.view(np.uint32)):
+            return False
+    # the ragged end too
+    exp = oracle.pipelined_map(xs[n - 1000:], op, threads=1)
+    return bool(np.array_equal(y_dev[n - 1000:].cpu().numpy().view(np.uint32), exp.view(np.uint32)))
+
+
+def cpu_baseline(x_host, op, bytes_per_elem, seconds):
+    """The oracle (untuned) on this host's cores over the same input."""
+    import oracle
+    threads = oracle.default_threads()
+    xs = x_host.numpy()
+    out = xs.copy()
+    times = []
+    t_end = time.perf_counter() + seconds
+    while True:
+        t0 = time.perf_counter()
+        oracle.pipelined_map(xs, op, threads=threads, out=out)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() >= t_end or len(times) >= 50:
+            break
+    t = median(times)
+    return {"value": round(bytes_per_elem * xs.size / t / 1e9, 3), "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"full input ({xs.size} floats), {len(times)} passes, median pass {t * 1e3:.1f} ms"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the hot path needs no cross-GPU step and this "
+              "build runs on a single MI355X; use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import software_pipelining_amd as tp
+    from software_pipelining_amd import workloads
+
+    dev = torch.device("cuda:0")
+    tp.device_check(0)
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count} "
+        f"LDS/WG={tp.lds_budget(0)}")
+
+    # ---------------------------------------------------------- headline
+    n = 1 << 28
+    log("generating 2^28 inputs (seed 2)")
+    x_host = workloads.uniform_pm1(n, seed=2)
+    xbuf = torch.empty(n + 4, dtype=torch.float32, device=dev)
+    xbuf[:n].copy_(x_host)
+    xbuf[n:].zero_()
+    x = xbuf[:n]
+    y = torch.empty(n, dtype=torch.float32, device=dev)
+    S, T, TPB = args.stages, args.tile, args.tiles_per_block
+    alg_bytes = 8 * n
+    path = tp.pipelined_map(x, y, "scale2", T, S, TPB)
+    torch.cuda.synchronize()
+    parity = sampled_parity(x_host, y, "scale2")
+    log(f"headline parity (sampled windows vs oracle): {parity}")
+    per, region = time_launches(lambda: tp.pipelined_map(x, y, "scale2", T, S, TPB),
+                                args.warmup, args.steps)
+    ms_step = region / args.steps
+    value = alg_bytes / (ms_step * 1e-3) / 1e9
+    avg_launch = sum(per) / len(per)
+    achieved = alg_bytes / (avg_launch * 1e-3) / 1e9
+    log(f"headline: {value:.1f} GB/s ({100 * value / HBM_PEAK_GBS:.1f}% of peak), "
+        f"avg launch {avg_launch * 1e3:.1f} us")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"pipelined scale-by-2 map over 2^28 fp32 (1 GiB in, 1 GiB out), "
+                               f"uniform [-1,1) seed 2, tile {T} fp32, {S} stages, "
+                               f"{TPB} tiles per workgroup, 16-byte path",
+                   "n": n, "tile_elems": T, "stages": S, "tiles_per_block": TPB,
+                   "path": tp.Path(path).name.lower()},
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "parity": "bit-exact on sampled windows" if parity else "MISMATCH",
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": stored_traffic(f"map_scale2_n{n}_t{T}_s{S}"),
+                     "kernel": "map_kernel<scale2>", "algorithmic_bytes_per_launch": alg_bytes,
+                     "avg_launch_us": round(avg_launch * 1e3, 2)},
+    }
+
+    # copy ceiling for context: the runtime's device-to-device copy of 1 GiB
+    per_c, _ = time_launches(lambda: y.copy_(x), 3, 10)
+    result["copy_ceiling_GBs"] = round(alg_bytes / (median(per_c) * 1e-3) / 1e9, 1)
+
+    if not args.quick:
+        result["rows"] = extra_rows(args, tp, workloads, torch, np, dev, x_host, xbuf, y)
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle scale2 on the host cores")
+        result["cpu_baseline"] = cpu_baseline(x_host, "scale2", 8, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+def extra_rows(args, tp, workloads, torch, np, dev, x_host, xbuf, y):
+    rows = {}
+    n = x_host.numel()
+
+    # stage/tile sweep with the 4-byte source offset (misaligned fallback)
+    sweep = []
+    for off in (0, 1):
+        xin = xbuf[off:off + n]
+        for T in (256, 1024, 4096):
+            for S in (1, 2, 3, 4):
+                p = tp.pipelined_map(xin, y, "scale2", T, S, 64)
+                per, _ = time_launches(lambda: tp.pipelined_map(xin, y, "scale2", T, S, 64), 2, 8)
+                gbs = 8 * n / (median(per) * 1e-3) / 1e9
+                sweep.append({"src_offset_bytes": 4 * off, "tile": T, "stages": S,
+                              "path": tp.Path(p).name.lower(), "GBs": round(gbs, 1),
+                              "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1)})
+        log(f"sweep offset {4 * off}B done")
+    # parity of the last (fallback) point
+    rows["sweep_parity_offset4"] = bool(sampled_parity(torch.cat([x_host[1:], torch.zeros(1)])[:n], y,
+                                                       "scale2"))
+    rows["scale2_sweep"] = sweep
+
+    # small double-buffered map: 2^24, tile 256, 2 stages, 64 tiles per workgroup
+    ns = 1 << 24
+    xs_host = workloads.uniform_pm1(ns, seed=1)
+    xs = xs_host.to(dev)
+    ys = torch.empty_like(xs)
+    per, _ = time_launches(lambda: tp.pipelined_map(xs, ys, "scale2", 256, 2, 64), 5, 50)
+    gbs = 8 * ns / (median(per) * 1e-3) / 1e9
+    rows["scale2_small"] = {"n": ns, "tile": 256, "stages": 2, "GBs": round(gbs, 1),
+                            "note": "128 MiB footprint fits the 256 MB Infinity Cache: cache-warm"}
+    del xs, ys
+
+    # compute-heavy map: 2^27, horner32, tile 1024, stages 1/2/4
+    nh = 1 << 27
+    xh_host = workloads.uniform_pm1(nh, seed=4)
+    xh = xh_host.to(dev)
+    yh = torch.empty_like(xh)
+    hr = {}
+    for S in (1, 2, 4):
+        tp.pipelined_map(xh, yh, "horner32", 1024, S, 64)
+        per, _ = time_launches(lambda: tp.pipelined_map(xh, yh, "horner32", 1024, S, 64), 3, 10)
+        t = median(per) * 1e-3
+        hr[f"S{S}"] = {"GBs": round(8 * nh / t / 1e9, 1), "TFLOPs": round(64 * nh / t / 1e12, 2),
+                       "us": round(t * 1e6, 1)}
+    hr["speedup_S2_over_S1"] = round(hr["S1"]["us"] / hr["S2"]["us"], 3)
+    hr["speedup_S4_over_S1"] = round(hr["S1"]["us"] / hr["S4"]["us"], 3)
+    hr["parity"] = bool(sampled_parity(xh_host, yh, "horner32"))
+    rows["horner32"] = hr
+    log(f"horner32: {hr}")
+    del xh, yh
+
+    # predicated chunk copy: 2^26 chunks. Not timed on the GPU in this test
+    # window (it faulted twice before its wait-state hazard was found and fixed).
+    rows["chunk_copy"] = {"n_chunks": 1 << 26, "status": "not run on the GPU in this test window"}
+
+    # row exchange 64x4 (launch-bound)
+    a = workloads.arange_rows(64).to(dev)
+    b = torch.empty_like(a)
+    per, region = time_launches(lambda: tp.row_shift(a, b), 10, 1000)
+    rows["row_shift"] = {"rows": 64, "median_launch_us": round(median(per) * 1e3, 2),
+                         "region_us_per_call": round(region, 4)}
+    return rows
+
+
+if __name__ == "__main__":
+    main()

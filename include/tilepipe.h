@@ -1,0 +1,184 @@
+/*
+ * libtilepipe: software-pipelined global->LDS tile streaming on MI355X (gfx950).
+ *
+ * C ABI. Plain pointers and sizes only; HIP types are hidden behind void* so a
+ * caller needs no HIP headers. Every compute entry point is stream-ordered: it
+ * validates its arguments on the host, enqueues one kernel on `stream` and
+ * returns without synchronizing (the pages' copy interface likewise returns at
+ * once and completion is observed later: "Asynchronous Data Movement",
+ * section "cuda::memcpy_async"). Completion and any device fault are observed
+ * through the stream (hipStreamSynchronize, an event, or a later blocking
+ * call), as for any other stream operation.
+ *
+ * Conventions shared by all entry points
+ *  - Ownership: the caller owns every buffer (device memory from hipMalloc,
+ *    torch, or any allocator). The library never allocates, frees, or
+ *    synchronizes, and keeps no state other than a per-device cache of device
+ *    properties, so calls from several host threads are safe.
+ *  - Errors: argument errors are found on the host before anything is
+ *    enqueued; the call then returns a nonzero tp_status and enqueues nothing.
+ *    A failed launch returns TP_ERR_HIP; tp_last_hip_error() then gives the
+ *    hipError_t value (per calling thread). A device that is not gfx950 gives
+ *    TP_ERR_UNSUPPORTED_DEVICE. An empty problem (n == 0) returns TP_OK and
+ *    launches nothing.
+ *  - Alignment: float and chunk buffers must be 4-byte aligned
+ *    (TP_ERR_MISALIGNED otherwise). A buffer that is 4- but not 16-byte
+ *    aligned is not an error: it selects the element-wise (4-byte) fallback
+ *    for that side of the copy, and the choice is reported through path_out
+ *    (the pages' fallback is silent: "Asynchronous Data Movement", section
+ *    "Alignment requirements"; here it is observable). Results never depend on
+ *    the path.
+ *  - Aliasing: an output may be exactly the same buffer as the input (every
+ *    unit is read into LDS before it is written). Any partial overlap between
+ *    an output and another argument is TP_ERR_OVERLAP.
+ *  - `stream` is a hipStream_t (NULL = the null stream of the current device).
+ *    Kernels run on the device that is current on the calling thread.
+ *  - path_out (may be NULL) receives a tp_path value for the launch made.
+ */
+#ifndef TILEPIPE_H
+#define TILEPIPE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TP_API __attribute__((visibility("default")))
+
+#define TP_VERSION 1
+
+typedef enum tp_status {
+    TP_OK = 0,
+    TP_ERR_INVALID_ARG = 1,        /* null pointer, negative size, value out of range */
+    TP_ERR_MISALIGNED = 2,         /* a float/chunk buffer not 4-byte aligned */
+    TP_ERR_LDS_BUDGET = 3,         /* stages x tile bytes exceeds the device's LDS per workgroup */
+    TP_ERR_OVERLAP = 4,            /* output partially overlaps another argument */
+    TP_ERR_UNSUPPORTED_DEVICE = 5, /* current device is not gfx950 */
+    TP_ERR_HIP = 6                 /* a HIP runtime call or launch failed */
+} tp_status;
+
+typedef enum tp_op {
+    TP_OP_SCALE2 = 0,   /* y = 2 * x */
+    TP_OP_HORNER32 = 1, /* y = 0; for k = 0..31: y = fma(y, x, c_k), c_k = RN(1/(k+1)) */
+    TP_OP_COPY = 2      /* y = x (copy-bandwidth ceiling) */
+} tp_op;
+
+/* Which side of the copy uses 16-byte accesses: bit 0 set = loads use the
+ * 4-byte fallback (source not 16-byte aligned), bit 1 set = stores do. */
+typedef enum tp_path {
+    TP_PATH_X4 = 0,
+    TP_PATH_SCALAR_LOAD = 1,
+    TP_PATH_SCALAR_STORE = 2,
+    TP_PATH_SCALAR = 3
+} tp_path;
+
+/* Launch plan of one call: what the entry point would enqueue (host-only). */
+typedef struct tp_plan {
+    int32_t path;            /* tp_path */
+    int32_t stages;          /* LDS ring slots S (1 = no overlap inside a workgroup) */
+    int32_t tile_units;      /* floats per tile (map), chunks per tile (chunk copy), rows (row shift) */
+    int32_t threads;         /* workgroup size */
+    int32_t lane_chunks;     /* 16-byte chunks each lane moves per tile */
+    int32_t tiles_per_block; /* consecutive tiles one workgroup streams */
+    int32_t lds_bytes;       /* dynamic LDS per workgroup */
+    int32_t wait_steady;     /* vmcnt immediate of the steady-state stage wait */
+    int64_t num_tiles;       /* tiles over the whole problem */
+    int64_t grid;            /* workgroups launched (0: nothing to launch) */
+} tp_plan;
+
+/* Human-readable name of a tp_status value ("TP_OK", ...); never NULL. */
+TP_API const char *tp_status_string(int status);
+
+/* hipError_t of the last TP_ERR_HIP returned on the calling thread (0 if none). */
+TP_API int tp_last_hip_error(void);
+
+/* Library ABI version (TP_VERSION). */
+TP_API int tp_version(void);
+
+/* TP_OK if `device` is a gfx950 GPU, TP_ERR_UNSUPPORTED_DEVICE if it is another
+ * GPU, TP_ERR_HIP if it cannot be queried (no such device, no driver). The
+ * asynchronous-copy path exists only on hardware that has it ("Asynchronous
+ * Data Movement", section "Genuinely asynchronous from CC 8.0+"); this library
+ * targets only gfx950 and refuses other devices instead of degrading. */
+TP_API int tp_device_check(int device);
+
+/* Bytes of LDS one workgroup may use on `device` (written to *bytes), the
+ * budget the entry points check stages x tile bytes against. Returns TP_OK or
+ * TP_ERR_HIP; bytes must not be NULL (TP_ERR_INVALID_ARG). */
+TP_API int tp_device_lds_budget(int device, int64_t *bytes);
+
+/*
+ * Neighbour-row exchange ("Asynchronous Copies", section "A Global-to-Shared
+ * Copy"): each lane copies its 16-byte row of A into LDS asynchronously, waits
+ * for its copies, synchronizes the workgroup, then writes row (i+1) mod rows:
+ *     b[i][j] = a[(i + 1) % rows][j],   0 <= i < rows, 0 <= j < 4.
+ * a, b: device buffers of rows x 4 float32, row-major (16 bytes per row); data
+ * moves as raw 32-bit words. 0 <= rows <= 1024 (one workgroup; rows > 1024 is
+ * TP_ERR_INVALID_ARG). b == a is allowed (in place).
+ */
+TP_API int tp_row_shift(const float *a, float *b, int64_t rows, void *stream, int *path_out);
+
+/*
+ * Software-pipelined tiled map ("Asynchronous Data Movement", sections
+ * "Double buffering" and "Barriers and pipelines"; "CUDA Async Copy and
+ * Pipeline Guide", section "Implementation Comparison"):
+ *     out[i] = op(in[i]),   0 <= i < n.
+ * Each workgroup streams tiles_per_block consecutive tiles of tile_elems
+ * floats through an LDS ring of `stages` slots: the loads of the next
+ * stages-1 tiles are in flight while the current tile is computed on and
+ * stored. in, out: device buffers of n float32. op: tp_op.
+ * tile_elems: 256, 512, 1024, 2048, 4096 or 8192. stages: 1..8 ("Typically 2-4
+ * stages": the guide's FAQ; 1 = load, wait, compute, store with no overlap).
+ * tiles_per_block: 1..65536, or 0 for the default 64.
+ * stages * tile_elems * 4 must fit the device's LDS per workgroup
+ * (TP_ERR_LDS_BUDGET). out == in is allowed. The result does not depend on
+ * tile_elems, stages, tiles_per_block or the path.
+ */
+TP_API int tp_pipelined_map(const float *in, float *out, int64_t n, int op,
+                            int tile_elems, int stages, int tiles_per_block,
+                            void *stream, int *path_out);
+
+/*
+ * Predicated 16-byte chunk copy ("Asynchronous Copies", section "A
+ * Global-to-Shared Copy", the paragraph on pred, src_size and ignore_src).
+ * For each chunk i < n_chunks:
+ *   pred[i] == 0           -> dst chunk i is not written at all;
+ *   else ignore_src[i] != 0 -> dst chunk i = 16 zero bytes;
+ *   else                    -> dst bytes [0, s) = src bytes [0, s), bytes
+ *                              [s, 16) = 0, with s = min(src_size[i], 16).
+ * src, dst: device buffers of n_chunks x 16 bytes (4-byte aligned; 16-byte
+ * alignment selects the fast path). pred, src_size, ignore_src: device arrays
+ * of n_chunks bytes (any alignment), or NULL for "all 1", "all 16" and "all 0".
+ * The whole 16-byte source chunk must be readable memory whatever the operands
+ * say (the paragraph's bounds-check sentence); the kernel may read it. stages:
+ * 1..8. tiles_per_block (256-chunk tiles): 1..65536, or 0 for the default 64.
+ * dst == src is allowed; dst overlapping a metadata array is TP_ERR_OVERLAP.
+ */
+TP_API int tp_chunk_copy(const void *src, void *dst, int64_t n_chunks,
+                         const uint8_t *pred, const uint8_t *src_size,
+                         const uint8_t *ignore_src, int stages, int tiles_per_block,
+                         void *stream, int *path_out);
+
+/*
+ * Host-only planning: the same validation and launch plan as the entry point
+ * of the same name, for the given pointer values and LDS budget (bytes per
+ * workgroup), without touching any device. Pointers are only inspected for
+ * null, alignment and overlap. Returns the status the entry point would return
+ * for argument errors; on TP_OK, *plan describes the launch (plan may be NULL).
+ */
+TP_API int tp_plan_row_shift(const void *a, const void *b, int64_t rows,
+                             int64_t lds_budget, tp_plan *plan);
+TP_API int tp_plan_pipelined_map(const void *in, const void *out, int64_t n, int op,
+                                 int tile_elems, int stages, int tiles_per_block,
+                                 int64_t lds_budget, tp_plan *plan);
+TP_API int tp_plan_chunk_copy(const void *src, const void *dst, int64_t n_chunks,
+                              const void *pred, const void *src_size,
+                              const void *ignore_src, int stages, int tiles_per_block,
+                              int64_t lds_budget, tp_plan *plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TILEPIPE_H */

@@ -1,1 +1,16 @@
-"""libtilepipe: software-pipelined global->LDS tile streaming for MI355X (gfx950)."""
+"""libtilepipe: software-pipelined global->LDS tile streaming for MI355X (gfx950).
+
+The compute lives in hand-written HIP kernels inside ``libtilepipe.so`` behind a
+C ABI (``include/tilepipe.h``). :mod:`software_pipelining_amd.tilepipe` is the
+thin ctypes binding; it loads the library on first use and raises if it has not
+been built; there is no CPU fallback.
+"""
+from .tilepipe import (  # noqa: F401
+    TilepipeError, Path, Plan, chunk_copy, device_check, lds_budget, library_path,
+    pipelined_map, plan_chunk_copy, plan_map, plan_row_shift, row_shift,
+)
+
+__all__ = [
+    "TilepipeError", "Path", "Plan", "chunk_copy", "device_check", "lds_budget", "library_path",
+    "pipelined_map", "plan_chunk_copy", "plan_map", "plan_row_shift", "row_shift",
+]

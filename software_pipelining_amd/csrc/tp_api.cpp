@@ -1,0 +1,229 @@
+// C ABI of libtilepipe: validation, device checks and launches.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <stdint.h>
+#include <string.h>
+
+#include "tp_internal.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+struct DeviceInfo {
+    bool known;
+    int status;            // TP_OK or TP_ERR_UNSUPPORTED_DEVICE
+    int64_t lds_budget;    // bytes of LDS one workgroup may use
+};
+
+constexpr int kMaxDevices = 64;
+std::mutex g_mutex;
+DeviceInfo g_devices[kMaxDevices];
+
+int hip_failure(hipError_t e)
+{
+    g_last_hip_error = (int)e;
+    return TP_ERR_HIP;
+}
+
+// gfx950 only: the arch name is "gfx950" optionally followed by ":feature..."
+bool is_gfx950(const char *arch)
+{
+    return strncmp(arch, "gfx950", 6) == 0 && (arch[6] == '\0' || arch[6] == ':');
+}
+
+int query_device(int device, int64_t *lds_budget)
+{
+    if (device < 0 || device >= kMaxDevices)
+        return hip_failure(hipErrorInvalidDevice);
+    {
+        std::lock_guard<std::mutex> lock(g_mutex);
+        if (g_devices[device].known) {
+            if (lds_budget)
+                *lds_budget = g_devices[device].lds_budget;
+            return g_devices[device].status;
+        }
+    }
+    hipDeviceProp_t prop;
+    hipError_t e = hipGetDeviceProperties(&prop, device);
+    if (e != hipSuccess)
+        return hip_failure(e);
+    int lds = 0;
+    e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, device);
+    if (e != hipSuccess)
+        return hip_failure(e);
+    DeviceInfo info{true, is_gfx950(prop.gcnArchName) ? TP_OK : TP_ERR_UNSUPPORTED_DEVICE, lds};
+    {
+        std::lock_guard<std::mutex> lock(g_mutex);
+        g_devices[device] = info;
+    }
+    if (lds_budget)
+        *lds_budget = info.lds_budget;
+    return info.status;
+}
+
+int current_device(int64_t *lds_budget)
+{
+    int device = 0;
+    const hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess)
+        return hip_failure(e);
+    return query_device(device, lds_budget);
+}
+
+int finish_launch(int hip_error)
+{
+    if (hip_error != 0) {
+        (void)hipGetLastError();
+        return hip_failure((hipError_t)hip_error);
+    }
+    return TP_OK;
+}
+
+// Argument errors are decided with an unlimited LDS budget first, so a bad
+// call never touches the device; the device's real budget is checked after.
+constexpr int64_t kNoBudget = INT64_MAX;
+
+}  // namespace
+
+extern "C" {
+
+TP_API const char *tp_status_string(int status)
+{
+    switch (status) {
+    case TP_OK: return "TP_OK";
+    case TP_ERR_INVALID_ARG: return "TP_ERR_INVALID_ARG";
+    case TP_ERR_MISALIGNED: return "TP_ERR_MISALIGNED";
+    case TP_ERR_LDS_BUDGET: return "TP_ERR_LDS_BUDGET";
+    case TP_ERR_OVERLAP: return "TP_ERR_OVERLAP";
+    case TP_ERR_UNSUPPORTED_DEVICE: return "TP_ERR_UNSUPPORTED_DEVICE";
+    case TP_ERR_HIP: return "TP_ERR_HIP";
+    default: return "TP_ERR_UNKNOWN";
+    }
+}
+
+TP_API int tp_last_hip_error(void) { return g_last_hip_error; }
+
+TP_API int tp_version(void) { return TP_VERSION; }
+
+TP_API int tp_device_check(int device) { return query_device(device, nullptr); }
+
+TP_API int tp_device_lds_budget(int device, int64_t *bytes)
+{
+    if (!bytes)
+        return TP_ERR_INVALID_ARG;
+    const int st = query_device(device, bytes);
+    return st == TP_ERR_UNSUPPORTED_DEVICE ? TP_OK : st;
+}
+
+TP_API int tp_plan_row_shift(const void *a, const void *b, int64_t rows, int64_t lds_budget,
+                             tp_plan *plan)
+{
+    return tp::plan_row_shift((uintptr_t)a, (uintptr_t)b, rows, lds_budget, plan);
+}
+
+TP_API int tp_plan_pipelined_map(const void *in, const void *out, int64_t n, int op,
+                                 int tile_elems, int stages, int tiles_per_block,
+                                 int64_t lds_budget, tp_plan *plan)
+{
+    return tp::plan_map((uintptr_t)in, (uintptr_t)out, n, op, tile_elems, stages, tiles_per_block,
+                        lds_budget, plan);
+}
+
+TP_API int tp_plan_chunk_copy(const void *src, const void *dst, int64_t n_chunks,
+                              const void *pred, const void *src_size, const void *ignore_src,
+                              int stages, int tiles_per_block, int64_t lds_budget, tp_plan *plan)
+{
+    return tp::plan_chunk_copy((uintptr_t)src, (uintptr_t)dst, n_chunks, (uintptr_t)pred,
+                               (uintptr_t)src_size, (uintptr_t)ignore_src, stages,
+                               tiles_per_block, lds_budget, plan);
+}
+
+TP_API int tp_row_shift(const float *a, float *b, int64_t rows, void *stream, int *path_out)
+{
+    tp_plan plan;
+    int st = tp::plan_row_shift((uintptr_t)a, (uintptr_t)b, rows, kNoBudget, &plan);
+    if (st != TP_OK)
+        return st;
+    if (path_out)
+        *path_out = plan.path;
+    if (plan.grid == 0)
+        return TP_OK;
+    int64_t lds = 0;
+    if ((st = current_device(&lds)) != TP_OK)
+        return st;
+    if (plan.lds_bytes > lds)
+        return TP_ERR_LDS_BUDGET;
+    tp::RowShiftParams p{a, b, (int32_t)rows, 0};
+    return finish_launch(tp::launch_row_shift(plan, p, stream));
+}
+
+TP_API int tp_pipelined_map(const float *in, float *out, int64_t n, int op, int tile_elems,
+                            int stages, int tiles_per_block, void *stream, int *path_out)
+{
+    tp_plan plan;
+    int st = tp::plan_map((uintptr_t)in, (uintptr_t)out, n, op, tile_elems, stages,
+                          tiles_per_block, kNoBudget, &plan);
+    if (st != TP_OK)
+        return st;
+    if (path_out)
+        *path_out = plan.path;
+    if (plan.grid == 0)
+        return TP_OK;
+    int64_t lds = 0;
+    if ((st = current_device(&lds)) != TP_OK)
+        return st;
+    if (plan.lds_bytes > lds)
+        return TP_ERR_LDS_BUDGET;
+    tp::MapParams p;
+    memset(&p, 0, sizeof p);
+    p.in = in;
+    p.out = out;
+    p.n = n;
+    p.n_main = n & ~int64_t(3);
+    p.tiles_per_block = plan.tiles_per_block;
+    tp::horner32_coefficients(p.coef);
+    int e = 0;
+    switch (op) {
+    case TP_OP_SCALE2: e = tp::launch_map_scale2(plan, p, stream); break;
+    case TP_OP_HORNER32: e = tp::launch_map_horner32(plan, p, stream); break;
+    default: e = tp::launch_map_copy(plan, p, stream); break;
+    }
+    return finish_launch(e);
+}
+
+TP_API int tp_chunk_copy(const void *src, void *dst, int64_t n_chunks, const uint8_t *pred,
+                         const uint8_t *src_size, const uint8_t *ignore_src, int stages,
+                         int tiles_per_block, void *stream, int *path_out)
+{
+    tp_plan plan;
+    int st = tp::plan_chunk_copy((uintptr_t)src, (uintptr_t)dst, n_chunks, (uintptr_t)pred,
+                                 (uintptr_t)src_size, (uintptr_t)ignore_src, stages,
+                                 tiles_per_block, kNoBudget, &plan);
+    if (st != TP_OK)
+        return st;
+    if (path_out)
+        *path_out = plan.path;
+    if (plan.grid == 0)
+        return TP_OK;
+    int64_t lds = 0;
+    if ((st = current_device(&lds)) != TP_OK)
+        return st;
+    if (plan.lds_bytes > lds)
+        return TP_ERR_LDS_BUDGET;
+    tp::ChunkParams p;
+    memset(&p, 0, sizeof p);
+    p.src = static_cast<const uint8_t *>(src);
+    p.dst = static_cast<uint8_t *>(dst);
+    p.pred = pred;
+    p.src_size = src_size;
+    p.ignore_src = ignore_src;
+    p.n_chunks = n_chunks;
+    p.tiles_per_block = plan.tiles_per_block;
+    p.flags = (pred ? tp::kHasPred : 0) | (src_size ? tp::kHasSize : 0) |
+              (ignore_src ? tp::kHasIgnore : 0);
+    return finish_launch(tp::launch_chunk_copy(plan, p, stream));
+}
+
+}  // extern "C"

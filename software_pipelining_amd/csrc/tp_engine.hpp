@@ -1,0 +1,171 @@
+// Device-side building blocks of the global->LDS copy pipeline (gfx950 only).
+//
+// The pages build their pipelines from an asynchronous copy that returns at
+// once, a per-thread "wait until at most N of my copy groups are pending", and
+// a block barrier ("Asynchronous Copies", section "A Global-to-Shared Copy":
+// commit_group / wait_group / cta_sync; "Asynchronous Data Movement", section
+// "Barriers and pipelines": producer_commit / consumer_wait /
+// consumer_release). On CDNA4 those map onto:
+//
+//   asynchronous copy  -> buffer_load_{dword,dwordx4,ubyte} ... lds: the data
+//                         goes from memory straight into LDS at
+//                         M0 + lane * width, never through VGPRs;
+//   wait_group(N)      -> s_waitcnt vmcnt(N): a wave's vector-memory
+//                         operations retire in issue order, so "at most N
+//                         outstanding" means everything issued before the last
+//                         N has landed;
+//   cta_sync           -> s_barrier, after the wait, so every wave of the
+//                         workgroup sees every lane's LDS data.
+//
+// Every memory instruction here is inline assembly. The compiler therefore
+// never sees an LDS-DMA write (it would otherwise wait for all of them,
+// vmcnt(0), before every LDS read and serialize the pipeline), and the number
+// of memory instructions a wave issues is exactly what the wait counts assume.
+// Predication uses the buffer resource's range check instead of branches: a
+// lane whose offset is not below num_records moves no data (a load into LDS
+// writes zeros there, a store is dropped), yet the instruction still issues,
+// so counts never depend on data. Out-of-range offsets used here stay small:
+// at most a few tiles past num_records, never near 2^31.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tp {
+namespace dev {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource descriptor (V#) of a raw byte-addressed buffer: 48-bit base,
+// stride 0 (unstructured, range-checked against num_records in bytes), data
+// format 32-bit (word 3 = 0x00020000 on gfx9-family parts), no swizzle.
+struct BufferRes {
+    u32x4 d;
+};
+
+__device__ __forceinline__ BufferRes make_buffer_res(const void *base, uint32_t num_records)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    BufferRes r;
+    r.d.x = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    r.d.y = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xFFFFu);
+    r.d.z = __builtin_amdgcn_readfirstlane(num_records);
+    r.d.w = 0x00020000u;
+    return r;
+}
+
+// Byte address of a generic pointer into LDS, as the 32-bit LDS offset that
+// M0 and ds_* instructions take.
+__device__ __forceinline__ uint32_t lds_offset(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+__device__ __forceinline__ uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// The descriptor operand of a buffer instruction must live in SGPRs; this
+// keeps it there even if register allocation moved the value to VGPRs.
+__device__ __forceinline__ u32x4 sgpr_res(const BufferRes &r)
+{
+    return u32x4{uniform(r.d.x), uniform(r.d.y), uniform(r.d.z), uniform(r.d.w)};
+}
+
+// Lambdas that carry a kernel's per-tile steps are always inlined, so their
+// captures stay in registers.
+#define TP_INLINE __attribute__((always_inline))
+
+// ------------------------------------------------------ hazards (wait states)
+// The compiler's hazard recognizer cannot see inside inline assembly, so every
+// asm block below carries the wait states its buffer instruction needs:
+//   - a VALU write of an SGPR (e.g. the v_readfirstlane that rebuilds a
+//     descriptor the compiler kept in VGPRs) followed by a vector-memory
+//     instruction reading that SGPR needs 5 wait states: "s_nop 4" right
+//     before every buffer instruction;
+//   - an SALU write of M0 followed by an LDS-DMA load needs 1: the same nop;
+//   - a store of more than 8 bytes followed by a VALU write of its data VGPRs
+//     needs 1: "s_nop 0" right after every 16-byte store.
+
+// ------------------------------------------------------- async copies to LDS
+// Lane l's bytes land at LDS address m0 + l * width (m0 wave-uniform).
+// `voff` is the lane's byte offset inside the resource.
+__device__ __forceinline__ void dma_b128(const BufferRes &r, uint32_t voff, uint32_t m0)
+{
+    asm volatile("s_mov_b32 m0, %2\n\t"
+                 "s_nop 4\n\t"
+                 "buffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(sgpr_res(r)), "s"(m0)
+                 : "memory");
+}
+
+__device__ __forceinline__ void dma_b32(const BufferRes &r, uint32_t voff, uint32_t m0)
+{
+    asm volatile("s_mov_b32 m0, %2\n\t"
+                 "s_nop 4\n\t"
+                 "buffer_load_dword %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(sgpr_res(r)), "s"(m0)
+                 : "memory");
+}
+
+// One byte per lane; lane l's byte lands in the low byte of the dword at
+// m0 + 4 * l (LDS-DMA writes a dword slot per lane for sub-dword loads).
+__device__ __forceinline__ void dma_u8(const BufferRes &r, uint32_t voff, uint32_t m0)
+{
+    asm volatile("s_mov_b32 m0, %2\n\t"
+                 "s_nop 4\n\t"
+                 "buffer_load_ubyte %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(sgpr_res(r)), "s"(m0)
+                 : "memory");
+}
+
+// ----------------------------------------------------------------- stores
+// Streaming stores: the results are not read again by this kernel.
+__device__ __forceinline__ void store_b128(const BufferRes &r, uint32_t voff, u32x4 v)
+{
+    asm volatile("s_nop 4\n\t"
+                 "buffer_store_dwordx4 %0, %1, %2, 0 offen nt\n\t"
+                 "s_nop 0"
+                 :
+                 : "v"(v), "v"(voff), "s"(sgpr_res(r))
+                 : "memory");
+}
+
+__device__ __forceinline__ void store_b32(const BufferRes &r, uint32_t voff, uint32_t v)
+{
+    asm volatile("s_nop 4\n\t"
+                 "buffer_store_dword %0, %1, %2, 0 offen nt"
+                 :
+                 : "v"(v), "v"(voff), "s"(sgpr_res(r))
+                 : "memory");
+}
+
+// ------------------------------------------------------------ completion
+// Wait until at most K of this wave's vector-memory operations are pending.
+template <int K>
+__device__ __forceinline__ void vm_wait()
+{
+    static_assert(K >= 0 && K <= 63, "vmcnt is a 6-bit counter");
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(K) : "memory");
+}
+
+// Workgroup barrier; also a compiler barrier so no LDS access moves across it.
+__device__ __forceinline__ void block_sync()
+{
+    asm volatile("s_barrier" : : : "memory");
+}
+
+// ---------------------------------------------------------------- helpers
+template <int Begin, int End, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (Begin < End) {
+        f(std::integral_constant<int, Begin>{});
+        static_for<Begin + 1, End>(static_cast<F &&>(f));
+    }
+}
+
+}  // namespace dev
+}  // namespace tp

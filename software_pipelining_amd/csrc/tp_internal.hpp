@@ -1,0 +1,152 @@
+// Internal declarations shared by the host planner, the C ABI and the kernels.
+// Nothing here is part of the public ABI (that is include/tilepipe.h).
+#pragma once
+
+#include <stdint.h>
+
+#include "tilepipe.h"
+
+#if defined(__HIPCC__)
+#define TP_HD __host__ __device__
+#else
+#define TP_HD
+#endif
+
+namespace tp {
+
+constexpr int kMaxStages = 8;
+constexpr int kDefaultTilesPerBlock = 64;
+constexpr int kMaxTilesPerBlock = 65536;
+constexpr int kMaxRowShiftRows = 1024;
+constexpr int kChunkTile = 256;            // chunks per tile of the chunk copy (one per lane)
+constexpr int kChunkMetaArrays = 3;        // pred, src_size, ignore_src
+constexpr int kMapTailLdsBytes = 256;      // LDS area for the final partial 16-byte chunk
+constexpr int kVmcntMax = 63;              // vmcnt is a 6-bit counter on gfx9-family parts
+constexpr int64_t kMaxMapElems = int64_t(1) << 40;
+constexpr int64_t kMaxChunks = int64_t(1) << 36;
+constexpr int64_t kMaxRunBytes = int64_t(1) << 30;   // bytes one workgroup streams
+
+// Memory instructions each lane issues per tile of a pipelined loop.
+//   ld: loads per tile (LDS-DMA loads, plus metadata loads for the chunk copy)
+//   st: stores per tile
+// Wait count of the stage wait in iteration t of a loop with `stages` slots,
+// before tile t is consumed. Every load is issued unconditionally (tiles
+// outside a workgroup's range are out-of-range buffer loads that move no
+// data), so the number of memory instructions issued after tile t's last load
+// is fixed:
+//   loads of tiles t+1 .. t+S-2                    -> (S-2) * ld
+//   stores of the iterations issued after tile t   -> min(t, S-1) * st
+// Vector-memory operations of one wave retire in issue order on this
+// architecture (loads and stores share the single vmcnt counter), so
+// "at most that many outstanding" means tile t has landed in LDS. The count is
+// clamped to the counter's width; a smaller count only waits longer.
+TP_HD constexpr int stage_wait_count(int stages, int ld, int st, int t)
+{
+    const int after_loads = (stages - 2) * ld;
+    const int after_stores = (t < stages - 1 ? t : stages - 1) * st;
+    const int k = after_loads + after_stores;
+    return k > kVmcntMax ? kVmcntMax : (k < 0 ? 0 : k);
+}
+
+// ---------------------------------------------------------------- map
+struct MapGeometry {
+    int threads;      // workgroup size: min(256, tile_elems / 4)
+    int lane_chunks;  // L: 16-byte chunks per lane per tile
+};
+
+TP_HD constexpr MapGeometry map_geometry(int tile_elems)
+{
+    const int threads = tile_elems / 4 < 256 ? tile_elems / 4 : 256;
+    return MapGeometry{threads, tile_elems / (4 * threads)};
+}
+
+TP_HD constexpr int map_loads_per_tile(bool load_x4, int lane_chunks)
+{
+    return load_x4 ? lane_chunks : 4 * lane_chunks;
+}
+
+TP_HD constexpr int map_stores_per_tile(bool store_x4, int lane_chunks)
+{
+    return store_x4 ? lane_chunks : 4 * lane_chunks;
+}
+
+struct MapParams {
+    const float *in;
+    float *out;
+    int64_t n_main;          // elements in whole 16-byte chunks: n rounded down to a multiple of 4
+    int64_t n;               // all elements; [n_main, n) is the final partial chunk
+    int32_t tiles_per_block;
+    int32_t pad;
+    float coef[32];          // Horner coefficients (used by TP_OP_HORNER32 only)
+};
+
+// ---------------------------------------------------------- chunk copy
+TP_HD constexpr int chunk_loads_per_tile(bool load_x4)
+{
+    return kChunkMetaArrays + (load_x4 ? 1 : 4);
+}
+
+TP_HD constexpr int chunk_stores_per_tile(bool store_x4)
+{
+    return store_x4 ? 1 : 4;
+}
+
+TP_HD constexpr int chunk_meta_slots(int stages)
+{
+    return stages == 1 ? 1 : 2 * stages - 1;
+}
+
+constexpr int kChunkDataSlotBytes = kChunkTile * 16;                    // 4 KiB
+constexpr int kChunkMetaSlotBytes = kChunkMetaArrays * kChunkTile * 4;  // 3 KiB (4 bytes per lane)
+
+TP_HD constexpr int chunk_lds_bytes(int stages)
+{
+    return stages * kChunkDataSlotBytes + chunk_meta_slots(stages) * kChunkMetaSlotBytes;
+}
+
+enum ChunkFlags : int32_t {
+    kHasPred = 1,
+    kHasSize = 2,
+    kHasIgnore = 4,
+};
+
+struct ChunkParams {
+    const uint8_t *src;
+    uint8_t *dst;
+    const uint8_t *pred;
+    const uint8_t *src_size;
+    const uint8_t *ignore_src;
+    int64_t n_chunks;
+    int32_t tiles_per_block;
+    int32_t flags;           // ChunkFlags
+};
+
+// -------------------------------------------------------------- row shift
+struct RowShiftParams {
+    const float *a;
+    float *b;
+    int32_t rows;
+    int32_t pad;
+};
+
+// ---------------------------------------------------------- host planner
+// Pure host code (no HIP): argument validation and launch geometry.
+int plan_row_shift(uintptr_t a, uintptr_t b, int64_t rows, int64_t lds_budget, tp_plan *plan);
+int plan_map(uintptr_t in, uintptr_t out, int64_t n, int op, int tile_elems, int stages,
+             int tiles_per_block, int64_t lds_budget, tp_plan *plan);
+int plan_chunk_copy(uintptr_t src, uintptr_t dst, int64_t n_chunks, uintptr_t pred,
+                    uintptr_t src_size, uintptr_t ignore_src, int stages, int tiles_per_block,
+                    int64_t lds_budget, tp_plan *plan);
+
+// Horner coefficients c_k = RN(1/(k+1)), k = 0..31.
+void horner32_coefficients(float c[32]);
+
+// ------------------------------------------------------- kernel launchers
+// Each returns a hipError_t value (0 = success). `stream` is a hipStream_t.
+int launch_row_shift(const tp_plan &plan, const RowShiftParams &p, void *stream);
+int launch_map_scale2(const tp_plan &plan, const MapParams &p, void *stream);
+int launch_map_horner32(const tp_plan &plan, const MapParams &p, void *stream);
+int launch_map_copy(const tp_plan &plan, const MapParams &p, void *stream);
+int launch_chunk_copy(const tp_plan &plan, const ChunkParams &p, void *stream);
+
+}  // namespace tp

@@ -1,0 +1,250 @@
+// Software-pipelined tiled map: out[i] = op(in[i]).
+//
+// Schedule of one workgroup over its run of `cnt` consecutive tiles, with an
+// LDS ring of S slots ("Asynchronous Data Movement", section "Double
+// buffering": the first copy is issued before the loop, and each iteration
+// issues the next stage's copy before waiting on the current one; S slots
+// generalize the two buffers, the "N-buffering" of "CUDA Async Copy and
+// Pipeline Guide", section "Optimization Techniques"):
+//
+//   prologue   issue tiles 0 .. S-2 into slots 0 .. S-2
+//   iteration t:
+//     wait     vmcnt(k_t): this wave's loads of tile t have landed  (consumer_wait)
+//     barrier  every wave's part of tile t is visible; every wave has finished
+//              reading slot (t-1) mod S in iteration t-1              (consumer_release)
+//     issue    tile t+S-1 into slot (t+S-1) mod S = (t-1) mod S       (producer side)
+//     consume  read tile t from slot t mod S, apply op, store 16 bytes per lane
+//
+// so S-1 tiles are in flight while tile t is computed and stored. With S = 1
+// the loop degenerates to the classic load -> barrier -> compute -> barrier
+// ("Asynchronous Data Movement", opening paragraph). Tiles past the end of
+// the workgroup's run are still "issued" as out-of-range loads that move no
+// data: the count of memory instructions between tile t's loads and its wait
+// is then the same for every t, and k_t is a compile-time immediate (the
+// first S-1 iterations, whose loads were issued before any store, are peeled
+// with their own smaller counts).
+//
+// Layout: a tile is tile_elems contiguous floats of global memory and sits
+// contiguously in its LDS slot. With the 16-byte path, lane `tid` moves chunk
+// i*threads + tid (i < L) of the tile; with the 4-byte fallback it moves float
+// i*threads + tid (i < 4L). Loads and stores choose their width
+// independently from the alignment of `in` and `out`.
+#pragma once
+
+#include <array>
+#include <utility>
+
+#include "tp_engine.hpp"
+#include "tp_internal.hpp"
+
+namespace tp {
+namespace dev {
+
+template <int OP>
+struct MapOp;
+
+template <>
+struct MapOp<TP_OP_SCALE2> {
+    template <int N>
+    __device__ __forceinline__ static void apply(float (&v)[N], const float *)
+    {
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            v[i] = v[i] * 2.0f;
+    }
+};
+
+template <>
+struct MapOp<TP_OP_COPY> {
+    template <int N>
+    __device__ __forceinline__ static void apply(float (&)[N], const float *) {}
+};
+
+// y = 0; y = fma(y, x, c_k) for k = 0..31. The N elements of a lane form N
+// independent chains, interleaved so consecutive FMAs do not depend on each
+// other.
+template <>
+struct MapOp<TP_OP_HORNER32> {
+    template <int N>
+    __device__ __forceinline__ static void apply(float (&v)[N], const float *c)
+    {
+        float y[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            y[i] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+            const float ck = c[k];
+#pragma unroll
+            for (int i = 0; i < N; ++i)
+                y[i] = __builtin_fmaf(y[i], v[i], ck);
+        }
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            v[i] = y[i];
+    }
+};
+
+__device__ __forceinline__ uint32_t f2u(float x) { return __builtin_bit_cast(uint32_t, x); }
+
+template <int OP, int S, int L, bool LX4, bool SX4>
+__global__ void __launch_bounds__(256) map_kernel(MapParams p)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    constexpr int LD = map_loads_per_tile(LX4, L);
+    constexpr int ST = map_stores_per_tile(SX4, L);
+
+    const uint32_t nt = blockDim.x;
+    const uint32_t tid = threadIdx.x;
+    const uint32_t wave_first = uniform(tid & ~63u);
+    const uint32_t tile_bytes = nt * L * 16;
+    const int64_t tile_elems = (int64_t)nt * L * 4;
+    const int64_t first = (int64_t)blockIdx.x * p.tiles_per_block * tile_elems;
+    const int64_t rem = p.n_main - first;
+    const int64_t run_bytes = (int64_t)p.tiles_per_block * tile_bytes;
+    const uint32_t span = rem <= 0 ? 0u : (uint32_t)(rem * 4 < run_bytes ? rem * 4 : run_bytes);
+    const int cnt = (int)((span + tile_bytes - 1) / tile_bytes);
+    const int64_t base = rem > 0 ? first : 0;
+    const BufferRes rin = make_buffer_res(p.in + base, span);
+    const BufferRes rout = make_buffer_res(p.out + base, span);
+    const uint32_t ring = uniform(lds_offset(lds));
+
+    // Producer: copy tile j of the run into the LDS slot at byte address `slot`.
+    auto issue = [&](uint32_t j, uint32_t slot) TP_INLINE {
+        const uint32_t toff = j * tile_bytes;
+        if constexpr (LX4) {
+            static_for<0, L>([&](auto i) TP_INLINE {
+                dma_b128(rin, toff + (i * nt + tid) * 16, uniform(slot + (i * nt + wave_first) * 16));
+            });
+        } else {
+            static_for<0, 4 * L>([&](auto i) TP_INLINE {
+                dma_b32(rin, toff + (i * nt + tid) * 4, uniform(slot + (i * nt + wave_first) * 4));
+            });
+        }
+    };
+
+    // Consumer: tile j from the slot at LDS byte offset `slot_off` -> op -> store.
+    auto consume = [&](uint32_t j, uint32_t slot_off) TP_INLINE {
+        const uint32_t toff = j * tile_bytes;
+        float v[4 * L];
+        if constexpr (SX4) {
+            static_for<0, L>([&](auto i) TP_INLINE {
+                const f32x4 x = *reinterpret_cast<const f32x4 *>(lds + slot_off + (i * nt + tid) * 16);
+                v[4 * i + 0] = x.x;
+                v[4 * i + 1] = x.y;
+                v[4 * i + 2] = x.z;
+                v[4 * i + 3] = x.w;
+            });
+            MapOp<OP>::apply(v, p.coef);
+            static_for<0, L>([&](auto i) TP_INLINE {
+                const u32x4 o = {f2u(v[4 * i]), f2u(v[4 * i + 1]), f2u(v[4 * i + 2]), f2u(v[4 * i + 3])};
+                store_b128(rout, toff + (i * nt + tid) * 16, o);
+            });
+        } else {
+            static_for<0, 4 * L>([&](auto i) TP_INLINE {
+                v[i] = *reinterpret_cast<const float *>(lds + slot_off + (i * nt + tid) * 4);
+            });
+            MapOp<OP>::apply(v, p.coef);
+            static_for<0, 4 * L>([&](auto i) TP_INLINE { store_b32(rout, toff + (i * nt + tid) * 4, f2u(v[i])); });
+        }
+    };
+
+    if (cnt == 0) {
+        // only the final partial chunk (below) is left for this workgroup
+    } else if constexpr (S == 1) {
+        for (int t = 0; t < cnt; ++t) {
+            issue(t, ring);
+            vm_wait<0>();
+            block_sync();
+            consume(t, 0);
+            block_sync();
+        }
+    } else {
+        static_for<0, S - 1>([&](auto s) TP_INLINE { issue(s, ring + s * tile_bytes); });
+        bool stop = false;
+        static_for<0, S - 1>([&](auto T) TP_INLINE {
+            if (!stop) {
+                if ((int)T >= cnt) {
+                    stop = true;
+                } else {
+                    vm_wait<stage_wait_count(S, LD, ST, T)>();
+                    block_sync();
+                    issue(T + S - 1, ring + ((T + S - 1) % S) * tile_bytes);
+                    consume(T, (T % S) * tile_bytes);
+                }
+            }
+        });
+        uint32_t cur = (S - 1) % S;  // slot of tile t
+        for (int t = S - 1; t < cnt; ++t) {
+            const uint32_t nxt = cur == 0 ? S - 1 : cur - 1;  // slot of tile t + S - 1
+            vm_wait<stage_wait_count(S, LD, ST, S - 1)>();
+            block_sync();
+            issue(t + S - 1, ring + nxt * tile_bytes);
+            consume(t, cur * tile_bytes);
+            cur = cur + 1 == S ? 0 : cur + 1;
+        }
+    }
+
+    // The final partial 16-byte chunk (n not a multiple of 4): at most three
+    // floats, moved element-wise by the first wave of the last workgroup
+    // through an LDS area of its own.
+    if (p.n > p.n_main && blockIdx.x == gridDim.x - 1 && wave_first == 0) {
+        const uint32_t tail = (uint32_t)(p.n - p.n_main);
+        const BufferRes ti = make_buffer_res(p.in + p.n_main, tail * 4);
+        const BufferRes to = make_buffer_res(p.out + p.n_main, tail * 4);
+        const uint32_t tail_off = S * tile_bytes;
+        dma_b32(ti, tid * 4, uniform(ring + tail_off));
+        vm_wait<0>();
+        float v[1] = {*reinterpret_cast<const float *>(lds + tail_off + tid * 4)};
+        MapOp<OP>::apply(v, p.coef);
+        store_b32(to, tid * 4, f2u(v[0]));
+    }
+    // No copy into LDS may still be in flight when the workgroup's LDS is freed.
+    vm_wait<0>();
+}
+
+// Kernel table of one op: index ((S-1) * 4 + log2 L) * 4 + path.
+using MapKernelFn = void (*)(MapParams);
+
+template <int OP, int I>
+constexpr MapKernelFn map_entry()
+{
+    constexpr int path = I % 4;
+    constexpr int L = 1 << ((I / 4) % 4);
+    constexpr int S = I / 16 + 1;
+    return &map_kernel<OP, S, L, !(path & TP_PATH_SCALAR_LOAD), !(path & TP_PATH_SCALAR_STORE)>;
+}
+
+template <int OP, int... I>
+constexpr std::array<MapKernelFn, sizeof...(I)> map_table(std::integer_sequence<int, I...>)
+{
+    return {map_entry<OP, I>()...};
+}
+
+constexpr int map_table_index(int stages, int lane_chunks, int path)
+{
+    const int li = lane_chunks == 1 ? 0 : lane_chunks == 2 ? 1 : lane_chunks == 4 ? 2 : 3;
+    return ((stages - 1) * 4 + li) * 4 + path;
+}
+
+template <int OP>
+int launch_map_op(const tp_plan &plan, const MapParams &p, void *stream)
+{
+    static constexpr auto table = map_table<OP>(std::make_integer_sequence<int, kMaxStages * 4 * 4>{});
+    const MapKernelFn fn = table[map_table_index(plan.stages, plan.lane_chunks, plan.path)];
+    if (plan.lds_bytes > 65536) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 plan.lds_bytes);
+        if (e != hipSuccess)
+            return (int)e;
+    }
+    MapParams args = p;
+    void *kargs[] = {&args};
+    return (int)hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3((uint32_t)plan.grid),
+                                dim3((uint32_t)plan.threads), kargs, (size_t)plan.lds_bytes,
+                                (hipStream_t)stream);
+}
+
+}  // namespace dev
+}  // namespace tp

@@ -1,0 +1,179 @@
+// Host-side argument validation and launch planning. Pure C++: no HIP calls,
+// so every rule here can be exercised on a machine without a GPU.
+#include <string.h>
+
+#include "tp_internal.hpp"
+
+namespace tp {
+namespace {
+
+bool overlaps(uintptr_t a, uint64_t a_bytes, uintptr_t b, uint64_t b_bytes)
+{
+    if (a_bytes == 0 || b_bytes == 0)
+        return false;
+    return a < b + b_bytes && b < a + a_bytes;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int path_bits(uintptr_t load_ptr, uintptr_t store_ptr)
+{
+    return ((load_ptr % 16) ? TP_PATH_SCALAR_LOAD : 0) | ((store_ptr % 16) ? TP_PATH_SCALAR_STORE : 0);
+}
+
+bool valid_tile(int tile_elems)
+{
+    switch (tile_elems) {
+    case 256: case 512: case 1024: case 2048: case 4096: case 8192:
+        return true;
+    default:
+        return false;
+    }
+}
+
+int resolve_tiles_per_block(int tiles_per_block)
+{
+    if (tiles_per_block == 0)
+        return kDefaultTilesPerBlock;
+    if (tiles_per_block < 0 || tiles_per_block > kMaxTilesPerBlock)
+        return -1;
+    return tiles_per_block;
+}
+
+}  // namespace
+
+int plan_row_shift(uintptr_t a, uintptr_t b, int64_t rows, int64_t lds_budget, tp_plan *plan)
+{
+    if (rows < 0 || rows > kMaxRowShiftRows)
+        return TP_ERR_INVALID_ARG;
+    tp_plan p;
+    memset(&p, 0, sizeof p);
+    p.stages = 1;
+    p.tile_units = (int32_t)rows;
+    p.lane_chunks = 1;
+    p.tiles_per_block = 1;
+    if (rows > 0) {
+        if (!a || !b)
+            return TP_ERR_INVALID_ARG;
+        if (a % 4 || b % 4)
+            return TP_ERR_MISALIGNED;
+        const uint64_t bytes = (uint64_t)rows * 16;
+        if (a != b && overlaps(a, bytes, b, bytes))
+            return TP_ERR_OVERLAP;
+        p.threads = (int32_t)(ceil_div(rows, 64) * 64);
+        p.lds_bytes = p.threads * 16;
+        if (p.lds_bytes > lds_budget)
+            return TP_ERR_LDS_BUDGET;
+        p.path = path_bits(a, b);
+        p.num_tiles = 1;
+        p.grid = 1;
+    }
+    if (plan)
+        *plan = p;
+    return TP_OK;
+}
+
+int plan_map(uintptr_t in, uintptr_t out, int64_t n, int op, int tile_elems, int stages,
+             int tiles_per_block, int64_t lds_budget, tp_plan *plan)
+{
+    if (n < 0 || n > kMaxMapElems)
+        return TP_ERR_INVALID_ARG;
+    if (op != TP_OP_SCALE2 && op != TP_OP_HORNER32 && op != TP_OP_COPY)
+        return TP_ERR_INVALID_ARG;
+    if (!valid_tile(tile_elems) || stages < 1 || stages > kMaxStages)
+        return TP_ERR_INVALID_ARG;
+    const int tpb = resolve_tiles_per_block(tiles_per_block);
+    if (tpb < 0)
+        return TP_ERR_INVALID_ARG;
+    // a workgroup's run (plus S-1 tiles of out-of-range prefetch) must stay
+    // well inside 32-bit buffer offsets
+    if ((int64_t)tpb * tile_elems * 4 > kMaxRunBytes)
+        return TP_ERR_INVALID_ARG;
+    const MapGeometry g = map_geometry(tile_elems);
+    tp_plan p;
+    memset(&p, 0, sizeof p);
+    p.stages = stages;
+    p.tile_units = tile_elems;
+    p.threads = g.threads;
+    p.lane_chunks = g.lane_chunks;
+    p.tiles_per_block = tpb;
+    p.lds_bytes = stages * tile_elems * 4 + kMapTailLdsBytes;
+    if (n > 0) {
+        if (!in || !out)
+            return TP_ERR_INVALID_ARG;
+        if (in % 4 || out % 4)
+            return TP_ERR_MISALIGNED;
+        const uint64_t bytes = (uint64_t)n * 4;
+        if (in != out && overlaps(in, bytes, out, bytes))
+            return TP_ERR_OVERLAP;
+    }
+    if (p.lds_bytes > lds_budget)
+        return TP_ERR_LDS_BUDGET;
+    p.path = n > 0 ? path_bits(in, out) : TP_PATH_X4;
+    const bool load_x4 = !(p.path & TP_PATH_SCALAR_LOAD);
+    const bool store_x4 = !(p.path & TP_PATH_SCALAR_STORE);
+    p.wait_steady = stage_wait_count(stages, map_loads_per_tile(load_x4, g.lane_chunks),
+                                     map_stores_per_tile(store_x4, g.lane_chunks), stages);
+    const int64_t n_main = n & ~int64_t(3);
+    p.num_tiles = ceil_div(n_main, tile_elems);
+    p.grid = n == 0 ? 0 : (p.num_tiles == 0 ? 1 : ceil_div(p.num_tiles, tpb));
+    if (plan)
+        *plan = p;
+    return TP_OK;
+}
+
+int plan_chunk_copy(uintptr_t src, uintptr_t dst, int64_t n_chunks, uintptr_t pred,
+                    uintptr_t src_size, uintptr_t ignore_src, int stages, int tiles_per_block,
+                    int64_t lds_budget, tp_plan *plan)
+{
+    if (n_chunks < 0 || n_chunks > kMaxChunks)
+        return TP_ERR_INVALID_ARG;
+    if (stages < 1 || stages > kMaxStages)
+        return TP_ERR_INVALID_ARG;
+    const int tpb = resolve_tiles_per_block(tiles_per_block);
+    if (tpb < 0)
+        return TP_ERR_INVALID_ARG;
+    if ((int64_t)tpb * kChunkDataSlotBytes > kMaxRunBytes)
+        return TP_ERR_INVALID_ARG;
+    tp_plan p;
+    memset(&p, 0, sizeof p);
+    p.stages = stages;
+    p.tile_units = kChunkTile;
+    p.threads = kChunkTile;
+    p.lane_chunks = 1;
+    p.tiles_per_block = tpb;
+    p.lds_bytes = chunk_lds_bytes(stages);
+    if (n_chunks > 0) {
+        if (!src || !dst)
+            return TP_ERR_INVALID_ARG;
+        if (src % 4 || dst % 4)
+            return TP_ERR_MISALIGNED;
+        const uint64_t bytes = (uint64_t)n_chunks * 16;
+        if (src != dst && overlaps(src, bytes, dst, bytes))
+            return TP_ERR_OVERLAP;
+        const uintptr_t meta[3] = {pred, src_size, ignore_src};
+        for (uintptr_t m : meta)
+            if (m && overlaps(dst, bytes, m, (uint64_t)n_chunks))
+                return TP_ERR_OVERLAP;
+    }
+    if (p.lds_bytes > lds_budget)
+        return TP_ERR_LDS_BUDGET;
+    p.path = n_chunks > 0 ? path_bits(src, dst) : TP_PATH_X4;
+    const bool load_x4 = !(p.path & TP_PATH_SCALAR_LOAD);
+    const bool store_x4 = !(p.path & TP_PATH_SCALAR_STORE);
+    p.wait_steady = stage_wait_count(stages, chunk_loads_per_tile(load_x4),
+                                     chunk_stores_per_tile(store_x4), stages);
+    p.num_tiles = ceil_div(n_chunks, kChunkTile);
+    p.grid = ceil_div(p.num_tiles, tpb);
+    if (plan)
+        *plan = p;
+    return TP_OK;
+}
+
+void horner32_coefficients(float c[32])
+{
+    for (int k = 0; k < 32; ++k)
+        c[k] = 1.0f / (float)(k + 1);
+}
+
+}  // namespace tp

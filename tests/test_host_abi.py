@@ -1,0 +1,190 @@
+"""Host-side checks of libtilepipe that need no GPU: the shared library loads,
+exports every symbol include/tilepipe.h declares, and its planner enforces the
+documented argument rules (null pointers, sizes, alignment, overlap, LDS
+budget) and launch geometry. Only host-only calls are made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import software_pipelining_amd as tp
+from software_pipelining_amd import tilepipe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tilepipe.h")
+
+BIG = 1 << 62                 # "no LDS limit" for pure argument checks
+A = 0x7f0000000000            # fake, well-aligned device addresses
+B = 0x7f4000000000
+
+
+def _declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"TP_API\s+[\w\s\*]*?\b(tp_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = tilepipe._load()
+    names = _declared_symbols()
+    assert len(names) >= 10
+    for name in names:
+        assert hasattr(lib, name), name
+    assert lib.tp_version() == 1
+
+
+def test_status_strings():
+    lib = tilepipe._load()
+    for code, name in enumerate(tilepipe._STATUS):
+        assert lib.tp_status_string(code).decode() == name
+    assert lib.tp_status_string(99).decode() == "TP_ERR_UNKNOWN"
+
+
+def _status(fn, *args):
+    try:
+        fn(*args)
+        return 0
+    except tp.TilepipeError as e:
+        return e.status
+
+
+# ------------------------------------------------------------------ map
+def test_map_plan_geometry():
+    for tile, threads, lanes in [(256, 64, 1), (512, 128, 1), (1024, 256, 1), (2048, 256, 2),
+                                 (4096, 256, 4), (8192, 256, 8)]:
+        p = tp.plan_map(A, B, 1 << 20, "scale2", tile, 2, 0)
+        assert (p.threads, p.lane_chunks, p.tiles_per_block) == (threads, lanes, 64)
+        assert p.num_tiles == (1 << 20) // tile
+        assert p.grid == -(-p.num_tiles // 64)
+        assert p.lds_bytes == 2 * tile * 4 + 256
+        assert p.path == tp.Path.X4
+
+
+def test_map_plan_tail_and_small_sizes():
+    assert tp.plan_map(A, B, 0).grid == 0
+    p = tp.plan_map(A, B, 3, tile_elems=1024)
+    assert (p.num_tiles, p.grid) == (0, 1)          # tail-only launch
+    p = tp.plan_map(A, B, 1027, tile_elems=1024, tiles_per_block=1)
+    assert (p.num_tiles, p.grid) == (1, 1)          # one tile, then a 3-float tail
+    p = tp.plan_map(A, B, 1029, tile_elems=1024, tiles_per_block=1)
+    assert (p.num_tiles, p.grid) == (2, 2)          # a partial second tile, 1-float tail
+    p = tp.plan_map(A, B, (1 << 28), tile_elems=256, stages=2, tiles_per_block=64)
+    assert p.grid == 16384
+
+
+def test_map_plan_paths_follow_alignment():
+    assert tp.plan_map(A + 4, B, 100).path == tp.Path.SCALAR_LOAD
+    assert tp.plan_map(A, B + 8, 100).path == tp.Path.SCALAR_STORE
+    assert tp.plan_map(A + 12, B + 4, 100).path == tp.Path.SCALAR
+    assert tp.plan_map(A + 16, B + 32, 100).path == tp.Path.X4
+
+
+def test_map_plan_wait_counts():
+    # steady-state vmcnt: (S-2) loads + (S-1) stores per lane between a tile's
+    # load and its wait; 0 for S = 1; clamped to 63
+    assert tp.plan_map(A, B, 100, stages=1).wait_steady == 0
+    assert tp.plan_map(A, B, 100, stages=2).wait_steady == 1
+    assert tp.plan_map(A, B, 100, stages=4, tile_elems=4096).wait_steady == 2 * 4 + 3 * 4
+    assert tp.plan_map(A + 4, B, 100, stages=3, tile_elems=1024).wait_steady == 4 + 2
+    assert tp.plan_map(A + 4, B + 4, 100, stages=8, tile_elems=8192).wait_steady == 63
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, B, -1), 1),
+    ((0, B, 10), 1),
+    ((A, 0, 10), 1),
+    ((A + 2, B, 10), 2),
+    ((A, B + 1, 10), 2),
+    ((A, A + 4, 10), 4),          # partial overlap
+    ((A + 36, A, 10), 4),
+])
+def test_map_plan_argument_errors(args, status):
+    assert _status(tp.plan_map, *args) == status
+
+
+def test_map_plan_option_errors():
+    assert _status(tp.plan_map, A, B, 10, "nope") == 1
+    for tile in (0, 64, 128, 300, 16384):
+        assert _status(tp.plan_map, A, B, 10, "scale2", tile) == 1
+    for s in (0, 9, -1):
+        assert _status(tp.plan_map, A, B, 10, "scale2", 1024, s) == 1
+    assert _status(tp.plan_map, A, B, 10, "scale2", 1024, 2, -1) == 1
+    assert _status(tp.plan_map, A, B, 10, "scale2", 1024, 2, 65537) == 1
+    assert _status(tp.plan_map, A, B, 10, "scale2", 8192, 2, 65536) == 1   # run > 1 GiB
+    assert _status(tp.plan_map, A, B, 1 << 41) == 1
+    # exact aliasing is allowed; n == 0 accepts null pointers
+    assert tp.plan_map(A, A, 10).grid == 1
+    assert tp.plan_map(0, 0, 0).grid == 0
+
+
+def test_map_plan_lds_budget():
+    assert _status(tp.plan_map, A, B, 10, "scale2", 4096, 4, 0, 64 * 1024) == 3
+    assert tp.plan_map(A, B, 10, "scale2", 4096, 4, 0, 160 * 1024).lds_bytes == 4 * 16384 + 256
+    assert _status(tp.plan_map, A, B, 10, "scale2", 8192, 8, 0, 160 * 1024) == 3
+
+
+# ------------------------------------------------------------ row shift
+def test_row_shift_plan():
+    p = tp.plan_row_shift(A, B, 64)
+    assert (p.threads, p.grid, p.lds_bytes, p.path) == (64, 1, 1024, tp.Path.X4)
+    p = tp.plan_row_shift(A, B, 65)
+    assert (p.threads, p.lds_bytes) == (128, 2048)
+    assert tp.plan_row_shift(A + 4, B, 3).path == tp.Path.SCALAR_LOAD
+    assert tp.plan_row_shift(A, A, 1024).grid == 1
+    assert tp.plan_row_shift(0, 0, 0).grid == 0
+    assert _status(tp.plan_row_shift, A, B, 1025) == 1
+    assert _status(tp.plan_row_shift, A, B, -1) == 1
+    assert _status(tp.plan_row_shift, 0, B, 4) == 1
+    assert _status(tp.plan_row_shift, A + 1, B, 4) == 2
+    assert _status(tp.plan_row_shift, A, A + 16, 4) == 4
+
+
+# ----------------------------------------------------------- chunk copy
+def test_chunk_copy_plan():
+    p = tp.plan_chunk_copy(A, B, 1 << 26)
+    assert (p.threads, p.tile_units, p.num_tiles, p.grid) == (256, 256, 1 << 18, 1 << 12)
+    assert p.lds_bytes == 2 * 4096 + 3 * 3072
+    assert p.wait_steady == 0 * 4 + 1 * 1
+    assert tp.plan_chunk_copy(A, B, 10, stages=4).wait_steady == 2 * 4 + 3 * 1
+    assert tp.plan_chunk_copy(A + 4, B + 4, 10, stages=3).wait_steady == 1 * 7 + 2 * 4
+    assert tp.plan_chunk_copy(A + 4, B, 10).path == tp.Path.SCALAR_LOAD
+    assert tp.plan_chunk_copy(A, A, 10).grid == 1
+    assert tp.plan_chunk_copy(0, 0, 0).grid == 0
+
+
+def test_chunk_copy_plan_errors():
+    assert _status(tp.plan_chunk_copy, A, B, -1) == 1
+    assert _status(tp.plan_chunk_copy, 0, B, 1) == 1
+    assert _status(tp.plan_chunk_copy, A + 2, B, 1) == 2
+    assert _status(tp.plan_chunk_copy, A, A + 16, 4) == 4
+    # dst overlapping a metadata array
+    assert _status(tp.plan_chunk_copy, A, B, 100, B + 50) == 4
+    assert _status(tp.plan_chunk_copy, A, B, 100, 0, 0, B + 1599) == 4
+    assert tp.plan_chunk_copy(A, B, 100, B + 1600, A, A).grid == 1   # metadata may alias src
+    assert _status(tp.plan_chunk_copy, A, B, 1, 0, 0, 0, 9) == 1
+    assert _status(tp.plan_chunk_copy, A, B, 1, 0, 0, 0, 8, 0, 8 * 4096) == 3
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(16)
+    with pytest.raises(ValueError):
+        tp.pipelined_map(x, x.clone())
+    with pytest.raises(ValueError):
+        tp.row_shift(x.reshape(4, 4))
+    with pytest.raises(ValueError):
+        tp.chunk_copy(torch.zeros(16, dtype=torch.uint8), torch.zeros(16, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        tp.pipelined_map(x, x.clone(), op="bogus")
+
+
+def test_header_is_plain_c():
+    # the ABI header must compile as C without HIP headers
+    import subprocess
+    import tempfile
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "t.c")
+        with open(src, "w") as f:
+            f.write('#include "tilepipe.h"\nint main(void){tp_plan p; (void)p; return TP_OK;}\n')
+        subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", f"-I{ROOT}/include", "-c", src,
+                        "-o", os.path.join(d, "t.o")], check=True)
