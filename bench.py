@@ -34,12 +34,15 @@ def log(msg: str):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--stages", type=int, default=3)
-    ap.add_argument("--tile", type=int, default=4096)
-    ap.add_argument("--tiles-per-block", type=int, default=64)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--stages", type=int, default=2)
+    ap.add_argument("--tile", type=int, default=256)
+    ap.add_argument("--tiles-per-block", type=int, default=0,
+                    help="consecutive tiles per workgroup (0: the library default)")
     ap.add_argument("--quick", action="store_true", help="headline only: no sweep, no extra rows")
+    ap.add_argument("--mode", choices=("bench", "stages"), default="bench",
+                    help="stages: only run the maps at 1-4 stages (for hardware-counter passes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline")
@@ -70,6 +73,24 @@ def time_launches(fn, warmup: int, steps: int):
     torch.cuda.synchronize()
     per = [a.elapsed_time(b) for a, b in zip(starts, ends)]
     return per, r0.elapsed_time(r1)
+
+
+def time_region(fn, warmup: int, steps: int) -> float:
+    """Milliseconds for `steps` back-to-back calls after `warmup` untimed ones,
+    bracketed by two events on the current stream (no events in between)."""
+    import torch
+    s = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    r0 = torch.cuda.Event(enable_timing=True)
+    r1 = torch.cuda.Event(enable_timing=True)
+    r0.record(s)
+    for _ in range(steps):
+        fn()
+    r1.record(s)
+    torch.cuda.synchronize()
+    return r0.elapsed_time(r1)
 
 
 def median(v):
@@ -142,12 +163,33 @@ def cpu_baseline(x_host, op, bytes_per_elem, seconds):
             "sample": f"full input ({xs.size} floats), {len(times)} passes, median pass {t * 1e3:.1f} ms"}
 
 
+def stages_mode(args):
+    """Launch the maps at stages 1..4 with a fixed grid and occupancy (tile 1024,
+    16 tiles per workgroup), a few times each, for per-stage counter passes."""
+    import torch
+    import software_pipelining_amd as tp
+    from software_pipelining_amd import workloads
+    dev = torch.device("cuda:0")
+    for op, n, seed in (("horner32", 1 << 27, 4), ("scale2", 1 << 28, 2)):
+        x = workloads.uniform_pm1(n, seed=seed).to(dev)
+        y = torch.empty_like(x)
+        for S in (1, 2, 3, 4):
+            per, _ = time_launches(lambda: tp.pipelined_map(x, y, op, 1024, S, 16), 2, args.steps)
+            log(f"{op} tile 1024 T16 S{S}: {median(per) * 1e3:.1f} us")
+        del x, y
+    torch.cuda.synchronize()
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the hot path needs no cross-GPU step and this "
               "build runs on a single MI355X; use --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.mode == "stages":
+        stages_mode(args)
+        return
 
     import numpy as np
     import torch
@@ -173,11 +215,13 @@ def main():
     S, T, TPB = args.stages, args.tile, args.tiles_per_block
     alg_bytes = 8 * n
     path = tp.pipelined_map(x, y, "scale2", T, S, TPB)
+    plan = tp.plan_map(x.data_ptr(), y.data_ptr(), n, "scale2", T, S, TPB)
     torch.cuda.synchronize()
     parity = sampled_parity(x_host, y, "scale2")
     log(f"headline parity (sampled windows vs oracle): {parity}")
-    per, region = time_launches(lambda: tp.pipelined_map(x, y, "scale2", T, S, TPB),
-                                args.warmup, args.steps)
+    step = lambda: tp.pipelined_map(x, y, "scale2", T, S, TPB)
+    region = time_region(step, args.warmup, args.steps)          # the whole job, back to back
+    per, _ = time_launches(step, 2, args.steps)                   # per-launch kernel durations
     ms_step = region / args.steps
     value = alg_bytes / (ms_step * 1e-3) / 1e9
     avg_launch = sum(per) / len(per)
@@ -200,14 +244,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"pipelined scale-by-2 map over 2^28 fp32 (1 GiB in, 1 GiB out), "
                                f"uniform [-1,1) seed 2, tile {T} fp32, {S} stages, "
-                               f"{TPB} tiles per workgroup, 16-byte path",
-                   "n": n, "tile_elems": T, "stages": S, "tiles_per_block": TPB,
-                   "path": tp.Path(path).name.lower()},
+                               f"{plan.tiles_per_block} tiles per workgroup, 16-byte path",
+                   "n": n, "tile_elems": T, "stages": S, "tiles_per_block": plan.tiles_per_block,
+                   "grid": plan.grid, "path": tp.Path(path).name.lower()},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "parity": "bit-exact on sampled windows" if parity else "MISMATCH",
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": stored_traffic(f"map_scale2_n{n}_t{T}_s{S}"),
+                     "traffic": stored_traffic(f"map_scale2_n{n}_t{T}_s{S}_T{plan.tiles_per_block}"),
                      "kernel": "map_kernel<scale2>", "algorithmic_bytes_per_launch": alg_bytes,
                      "avg_launch_us": round(avg_launch * 1e3, 2)},
     }
@@ -237,8 +281,8 @@ def extra_rows(args, tp, workloads, torch, np, dev, x_host, xbuf, y):
         xin = xbuf[off:off + n]
         for T in (256, 1024, 4096):
             for S in (1, 2, 3, 4):
-                p = tp.pipelined_map(xin, y, "scale2", T, S, 64)
-                per, _ = time_launches(lambda: tp.pipelined_map(xin, y, "scale2", T, S, 64), 2, 8)
+                p = tp.pipelined_map(xin, y, "scale2", T, S, 0)
+                per, _ = time_launches(lambda: tp.pipelined_map(xin, y, "scale2", T, S, 0), 2, 8)
                 gbs = 8 * n / (median(per) * 1e-3) / 1e9
                 sweep.append({"src_offset_bytes": 4 * off, "tile": T, "stages": S,
                               "path": tp.Path(p).name.lower(), "GBs": round(gbs, 1),
@@ -260,21 +304,27 @@ def extra_rows(args, tp, workloads, torch, np, dev, x_host, xbuf, y):
                             "note": "128 MiB footprint fits the 256 MB Infinity Cache: cache-warm"}
     del xs, ys
 
-    # compute-heavy map: 2^27, horner32, tile 1024, stages 1/2/4
+    # compute-heavy map: 2^27, horner32, tile 1024, stages 1/2/4, at the
+    # library's run length and at 16 tiles per workgroup (fixed grid and
+    # occupancy across stages: 8 workgroups per CU either way)
     nh = 1 << 27
     xh_host = workloads.uniform_pm1(nh, seed=4)
     xh = xh_host.to(dev)
     yh = torch.empty_like(xh)
     hr = {}
-    for S in (1, 2, 4):
-        tp.pipelined_map(xh, yh, "horner32", 1024, S, 64)
-        per, _ = time_launches(lambda: tp.pipelined_map(xh, yh, "horner32", 1024, S, 64), 3, 10)
-        t = median(per) * 1e-3
-        hr[f"S{S}"] = {"GBs": round(8 * nh / t / 1e9, 1), "TFLOPs": round(64 * nh / t / 1e12, 2),
-                       "us": round(t * 1e6, 1)}
-    hr["speedup_S2_over_S1"] = round(hr["S1"]["us"] / hr["S2"]["us"], 3)
-    hr["speedup_S4_over_S1"] = round(hr["S1"]["us"] / hr["S4"]["us"], 3)
+    for tpb in (0, 16):
+        for S in (1, 2, 4):
+            tp.pipelined_map(xh, yh, "horner32", 1024, S, tpb)
+            per, _ = time_launches(lambda: tp.pipelined_map(xh, yh, "horner32", 1024, S, tpb), 3, 10)
+            t = median(per) * 1e-3
+            hr[f"T{tpb or 'default'}_S{S}"] = {"GBs": round(8 * nh / t / 1e9, 1),
+                                               "TFLOPs": round(64 * nh / t / 1e12, 2),
+                                               "us": round(t * 1e6, 1)}
+        key = f"T{tpb or 'default'}"
+        hr[f"{key}_speedup_S2_over_S1"] = round(hr[f"{key}_S1"]["us"] / hr[f"{key}_S2"]["us"], 3)
+        hr[f"{key}_speedup_S4_over_S1"] = round(hr[f"{key}_S1"]["us"] / hr[f"{key}_S4"]["us"], 3)
     hr["parity"] = bool(sampled_parity(xh_host, yh, "horner32"))
+    hr["fp32_valu_peak_TFLOPs"] = FP32_VALU_PEAK_TFLOPS
     rows["horner32"] = hr
     log(f"horner32: {hr}")
     del xh, yh

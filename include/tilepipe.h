@@ -130,7 +130,10 @@ TP_API int tp_row_shift(const float *a, float *b, int64_t rows, void *stream, in
  * stored. in, out: device buffers of n float32. op: tp_op.
  * tile_elems: 256, 512, 1024, 2048, 4096 or 8192. stages: 1..8 ("Typically 2-4
  * stages": the guide's FAQ; 1 = load, wait, compute, store with no overlap).
- * tiles_per_block: 1..65536, or 0 for the default 64.
+ * tiles_per_block: 1..65536, or 0 for the library default of 2 (the shortest
+ * run in which one tile's load overlaps the previous tile's compute; on
+ * MI355X short runs dispatched in order keep the memory traffic of all
+ * resident workgroups within a narrow window and stream fastest).
  * stages * tile_elems * 4 must fit the device's LDS per workgroup
  * (TP_ERR_LDS_BUDGET). out == in is allowed. The result does not depend on
  * tile_elems, stages, tiles_per_block or the path.

@@ -86,6 +86,19 @@ __device__ __forceinline__ u32x4 sgpr_res(const BufferRes &r)
 //   - a store of more than 8 bytes followed by a VALU write of its data VGPRs
 //     needs 1: "s_nop 0" right after every 16-byte store.
 
+// Cache-policy modifiers of the streaming loads and stores (compile-time).
+// Streamed data is touched once: loads are non-temporal, stores are
+// non-temporal at device scope (written through to memory rather than kept
+// dirty in the XCD's L2). Measured on the 2^28-float map: non-temporal LDS-DMA
+// loads move ~10 % more bytes per second than default-policy loads, and
+// device-scope stores a further 1-5 %.
+#ifndef TP_LOAD_CPOL
+#define TP_LOAD_CPOL " nt"
+#endif
+#ifndef TP_STORE_CPOL
+#define TP_STORE_CPOL " sc1 nt"
+#endif
+
 // ------------------------------------------------------- async copies to LDS
 // Lane l's bytes land at LDS address m0 + l * width (m0 wave-uniform).
 // `voff` is the lane's byte offset inside the resource.
@@ -93,7 +106,7 @@ __device__ __forceinline__ void dma_b128(const BufferRes &r, uint32_t voff, uint
 {
     asm volatile("s_mov_b32 m0, %2\n\t"
                  "s_nop 4\n\t"
-                 "buffer_load_dwordx4 %0, %1, 0 offen lds"
+                 "buffer_load_dwordx4 %0, %1, 0 offen" TP_LOAD_CPOL " lds"
                  :
                  : "v"(voff), "s"(sgpr_res(r)), "s"(m0)
                  : "memory");
@@ -103,7 +116,7 @@ __device__ __forceinline__ void dma_b32(const BufferRes &r, uint32_t voff, uint3
 {
     asm volatile("s_mov_b32 m0, %2\n\t"
                  "s_nop 4\n\t"
-                 "buffer_load_dword %0, %1, 0 offen lds"
+                 "buffer_load_dword %0, %1, 0 offen" TP_LOAD_CPOL " lds"
                  :
                  : "v"(voff), "s"(sgpr_res(r)), "s"(m0)
                  : "memory");
@@ -126,7 +139,7 @@ __device__ __forceinline__ void dma_u8(const BufferRes &r, uint32_t voff, uint32
 __device__ __forceinline__ void store_b128(const BufferRes &r, uint32_t voff, u32x4 v)
 {
     asm volatile("s_nop 4\n\t"
-                 "buffer_store_dwordx4 %0, %1, %2, 0 offen nt\n\t"
+                 "buffer_store_dwordx4 %0, %1, %2, 0 offen" TP_STORE_CPOL "\n\t"
                  "s_nop 0"
                  :
                  : "v"(v), "v"(voff), "s"(sgpr_res(r))
@@ -136,7 +149,7 @@ __device__ __forceinline__ void store_b128(const BufferRes &r, uint32_t voff, u3
 __device__ __forceinline__ void store_b32(const BufferRes &r, uint32_t voff, uint32_t v)
 {
     asm volatile("s_nop 4\n\t"
-                 "buffer_store_dword %0, %1, %2, 0 offen nt"
+                 "buffer_store_dword %0, %1, %2, 0 offen" TP_STORE_CPOL
                  :
                  : "v"(v), "v"(voff), "s"(sgpr_res(r))
                  : "memory");

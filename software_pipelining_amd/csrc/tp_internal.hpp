@@ -15,7 +15,8 @@
 namespace tp {
 
 constexpr int kMaxStages = 8;
-constexpr int kDefaultTilesPerBlock = 64;
+constexpr int kDefaultMapTilesPerBlock = 2;     // pipelined map, tiles_per_block == 0
+constexpr int kDefaultChunkTilesPerBlock = 64;  // chunk copy, tiles_per_block == 0
 constexpr int kMaxTilesPerBlock = 65536;
 constexpr int kMaxRowShiftRows = 1024;
 constexpr int kChunkTile = 256;            // chunks per tile of the chunk copy (one per lane)
@@ -75,7 +76,7 @@ struct MapParams {
     float *out;
     int64_t n_main;          // elements in whole 16-byte chunks: n rounded down to a multiple of 4
     int64_t n;               // all elements; [n_main, n) is the final partial chunk
-    int32_t tiles_per_block;
+    int32_t tiles_per_block; // consecutive tiles per workgroup
     int32_t pad;
     float coef[32];          // Horner coefficients (used by TP_OP_HORNER32 only)
 };

@@ -99,12 +99,15 @@ __global__ void __launch_bounds__(256) map_kernel(MapParams p)
     const uint32_t wave_first = uniform(tid & ~63u);
     const uint32_t tile_bytes = nt * L * 16;
     const int64_t tile_elems = (int64_t)nt * L * 4;
-    const int64_t first = (int64_t)blockIdx.x * p.tiles_per_block * tile_elems;
-    const int64_t rem = p.n_main - first;
+
+    // This workgroup's run: tiles [b T, (b + 1) T) of the input, tile j at
+    // byte j * tile_bytes of the resource window [base, base + span).
+    const int64_t run_first = (int64_t)blockIdx.x * p.tiles_per_block * tile_elems;
+    const int64_t rem = p.n_main - run_first;
     const int64_t run_bytes = (int64_t)p.tiles_per_block * tile_bytes;
     const uint32_t span = rem <= 0 ? 0u : (uint32_t)(rem * 4 < run_bytes ? rem * 4 : run_bytes);
+    const int64_t base = rem > 0 ? run_first : 0;
     const int cnt = (int)((span + tile_bytes - 1) / tile_bytes);
-    const int64_t base = rem > 0 ? first : 0;
     const BufferRes rin = make_buffer_res(p.in + base, span);
     const BufferRes rout = make_buffer_res(p.out + base, span);
     const uint32_t ring = uniform(lds_offset(lds));

@@ -31,10 +31,10 @@ bool valid_tile(int tile_elems)
     }
 }
 
-int resolve_tiles_per_block(int tiles_per_block)
+int resolve_tiles_per_block(int tiles_per_block, int default_value)
 {
     if (tiles_per_block == 0)
-        return kDefaultTilesPerBlock;
+        return default_value;
     if (tiles_per_block < 0 || tiles_per_block > kMaxTilesPerBlock)
         return -1;
     return tiles_per_block;
@@ -82,7 +82,7 @@ int plan_map(uintptr_t in, uintptr_t out, int64_t n, int op, int tile_elems, int
         return TP_ERR_INVALID_ARG;
     if (!valid_tile(tile_elems) || stages < 1 || stages > kMaxStages)
         return TP_ERR_INVALID_ARG;
-    const int tpb = resolve_tiles_per_block(tiles_per_block);
+    const int tpb = resolve_tiles_per_block(tiles_per_block, kDefaultMapTilesPerBlock);
     if (tpb < 0)
         return TP_ERR_INVALID_ARG;
     // a workgroup's run (plus S-1 tiles of out-of-range prefetch) must stay
@@ -130,7 +130,7 @@ int plan_chunk_copy(uintptr_t src, uintptr_t dst, int64_t n_chunks, uintptr_t pr
         return TP_ERR_INVALID_ARG;
     if (stages < 1 || stages > kMaxStages)
         return TP_ERR_INVALID_ARG;
-    const int tpb = resolve_tiles_per_block(tiles_per_block);
+    const int tpb = resolve_tiles_per_block(tiles_per_block, kDefaultChunkTilesPerBlock);
     if (tpb < 0)
         return TP_ERR_INVALID_ARG;
     if ((int64_t)tpb * kChunkDataSlotBytes > kMaxRunBytes)

@@ -166,7 +166,10 @@ def row_shift(a, b=None, stream=None) -> Path:
 
 def pipelined_map(x, y=None, op: str = "scale2", tile_elems: int = 1024, stages: int = 2,
                   tiles_per_block: int = 0, stream=None) -> Path:
-    """y[i] = op(x[i]) for float32 GPU tensors (any shape, contiguous)."""
+    """y[i] = op(x[i]) for float32 GPU tensors (any shape, contiguous).
+
+    Each workgroup streams tiles_per_block consecutive tiles (0: the
+    library default of 2)."""
     import torch
     if op not in OPS:
         raise ValueError(f"unknown op {op!r}; expected one of {sorted(OPS)}")

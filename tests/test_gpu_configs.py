@@ -51,10 +51,12 @@ def test_config3_stage_tile_sweep(cuda_device):
         xin = xbuf[off:off + n]
         for tile in (256, 1024, 4096):
             for stages in (1, 2, 3, 4):
-                y.fill_(float("nan"))
-                path = tp.pipelined_map(xin, y, "scale2", tile, stages, 64)
-                assert path == (tp.Path.SCALAR_LOAD if off else tp.Path.X4)
-                assert_equal_on_device(y, exp, f"config 3 offset={4 * off}B tile={tile} S={stages}")
+                for tpb in (0, 64):          # the library's run length (as benchmarked) and 64
+                    y.fill_(float("nan"))
+                    path = tp.pipelined_map(xin, y, "scale2", tile, stages, tpb)
+                    assert path == (tp.Path.SCALAR_LOAD if off else tp.Path.X4)
+                    assert_equal_on_device(y, exp, f"config 3 offset={4 * off}B tile={tile} "
+                                                   f"S={stages} T={tpb}")
         del exp
 
 
@@ -82,6 +84,7 @@ def test_config5_horner32(cuda_device):
     x = x_host.to(cuda_device)
     y = torch.empty_like(x)
     for stages in (1, 2, 4):
-        y.fill_(float("nan"))
-        tp.pipelined_map(x, y, "horner32", 1024, stages, 64)
-        assert_equal_on_device(y, exp, f"config 5 S={stages}")
+        for tpb in (0, 16, 64):
+            y.fill_(float("nan"))
+            tp.pipelined_map(x, y, "horner32", 1024, stages, tpb)
+            assert_equal_on_device(y, exp, f"config 5 S={stages} T={tpb}")

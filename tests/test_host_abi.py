@@ -49,10 +49,10 @@ def _status(fn, *args):
 
 
 # ------------------------------------------------------------------ map
-def test_map_plan_geometry():
+def test_map_plan_geometry_runs():
     for tile, threads, lanes in [(256, 64, 1), (512, 128, 1), (1024, 256, 1), (2048, 256, 2),
                                  (4096, 256, 4), (8192, 256, 8)]:
-        p = tp.plan_map(A, B, 1 << 20, "scale2", tile, 2, 0)
+        p = tp.plan_map(A, B, 1 << 20, "scale2", tile, 2, 64)
         assert (p.threads, p.lane_chunks, p.tiles_per_block) == (threads, lanes, 64)
         assert p.num_tiles == (1 << 20) // tile
         assert p.grid == -(-p.num_tiles // 64)
@@ -60,9 +60,18 @@ def test_map_plan_geometry():
         assert p.path == tp.Path.X4
 
 
+def test_map_plan_default_run_length():
+    p = tp.plan_map(A, B, 1 << 28, "scale2", 256, 2, 0)
+    assert p.tiles_per_block == 2 and p.grid == (1 << 20) // 2
+    p = tp.plan_map(A, B, 5000, "scale2", 1024, 2, 0)
+    assert (p.num_tiles, p.grid) == (5, 3)
+    p = tp.plan_chunk_copy(A, B, 1 << 26)
+    assert p.tiles_per_block == 64
+
+
 def test_map_plan_tail_and_small_sizes():
     assert tp.plan_map(A, B, 0).grid == 0
-    p = tp.plan_map(A, B, 3, tile_elems=1024)
+    p = tp.plan_map(A, B, 3, tile_elems=1024, tiles_per_block=64)
     assert (p.num_tiles, p.grid) == (0, 1)          # tail-only launch
     p = tp.plan_map(A, B, 1027, tile_elems=1024, tiles_per_block=1)
     assert (p.num_tiles, p.grid) == (1, 1)          # one tile, then a 3-float tail
@@ -111,6 +120,7 @@ def test_map_plan_option_errors():
     assert _status(tp.plan_map, A, B, 10, "scale2", 1024, 2, -1) == 1
     assert _status(tp.plan_map, A, B, 10, "scale2", 1024, 2, 65537) == 1
     assert _status(tp.plan_map, A, B, 10, "scale2", 8192, 2, 65536) == 1   # run > 1 GiB
+    assert _status(tp.plan_map, A, B, 10, "scale2", 1024, 2, -3) == 1
     assert _status(tp.plan_map, A, B, 1 << 41) == 1
     # exact aliasing is allowed; n == 0 accepts null pointers
     assert tp.plan_map(A, A, 10).grid == 1
