@@ -36,14 +36,16 @@ constexpr int64_t kMaxRunBytes = int64_t(1) << 30;   // bytes one workgroup stre
 // data), so the number of memory instructions issued after tile t's last load
 // is fixed:
 //   loads of tiles t+1 .. t+S-2                    -> (S-2) * ld
+//   (refill-first order: the refill of tile t+S-1 is issued before the wait,
+//    one more tile of loads                        -> (S-1) * ld)
 //   stores of the iterations issued after tile t   -> min(t, S-1) * st
 // Vector-memory operations of one wave retire in issue order on this
 // architecture (loads and stores share the single vmcnt counter), so
 // "at most that many outstanding" means tile t has landed in LDS. The count is
 // clamped to the counter's width; a smaller count only waits longer.
-TP_HD constexpr int stage_wait_count(int stages, int ld, int st, int t)
+TP_HD constexpr int stage_wait_count(int stages, int ld, int st, int t, bool refill_first = false)
 {
-    const int after_loads = (stages - 2) * ld;
+    const int after_loads = (stages - 2 + (refill_first ? 1 : 0)) * ld;
     const int after_stores = (t < stages - 1 ? t : stages - 1) * st;
     const int k = after_loads + after_stores;
     return k > kVmcntMax ? kVmcntMax : (k < 0 ? 0 : k);
@@ -69,6 +71,13 @@ TP_HD constexpr int map_loads_per_tile(bool load_x4, int lane_chunks)
 TP_HD constexpr int map_stores_per_tile(bool store_x4, int lane_chunks)
 {
     return store_x4 ? lane_chunks : 4 * lane_chunks;
+}
+
+// Loads and stores of the same width give every lane back exactly the bytes it
+// copied itself: the tile needs no exchange between waves.
+TP_HD constexpr bool map_wave_local(bool load_x4, bool store_x4)
+{
+    return load_x4 == store_x4;
 }
 
 struct MapParams {

@@ -1,28 +1,40 @@
 // Software-pipelined tiled map: out[i] = op(in[i]).
 //
-// Schedule of one workgroup over its run of `cnt` consecutive tiles, with an
-// LDS ring of S slots ("Asynchronous Data Movement", section "Double
-// buffering": the first copy is issued before the loop, and each iteration
-// issues the next stage's copy before waiting on the current one; S slots
-// generalize the two buffers, the "N-buffering" of "CUDA Async Copy and
-// Pipeline Guide", section "Optimization Techniques"):
+// A workgroup streams its run of `cnt` consecutive tiles through an LDS ring
+// of S slots ("Asynchronous Data Movement", section "Double buffering": the
+// first copy is issued before the loop, and each iteration issues the next
+// stage's copy before waiting on the current one; S slots generalize the two
+// buffers, the "N-buffering" of "CUDA Async Copy and Pipeline Guide", section
+// "Optimization Techniques"). Two schedules, chosen by the load/store widths:
 //
+// Refill-first (loads and stores of the same width). Every lane reads back
+// exactly the bytes it copied itself, so no wave needs another wave's data and
+// the slot a wave has just consumed is free for that wave at once:
+//   prologue   issue tiles 0 .. S-2 into slots 0 .. S-2
+//   iteration t:
+//     issue    tile t+S-1 into slot (t+S-1) mod S = (t-1) mod S   (just consumed)
+//     wait     vmcnt(k_t): this wave's loads of tile t have landed
+//     consume  read tile t from slot t mod S, apply op, store
+// so all S slots are loading while the wave waits for tile t.
+//
+// Exchange (a 16-byte side and a 4-byte side: lanes read bytes other waves
+// copied), the pages' protocol with a workgroup barrier:
 //   prologue   issue tiles 0 .. S-2 into slots 0 .. S-2
 //   iteration t:
 //     wait     vmcnt(k_t): this wave's loads of tile t have landed  (consumer_wait)
 //     barrier  every wave's part of tile t is visible; every wave has finished
 //              reading slot (t-1) mod S in iteration t-1              (consumer_release)
-//     issue    tile t+S-1 into slot (t+S-1) mod S = (t-1) mod S       (producer side)
-//     consume  read tile t from slot t mod S, apply op, store 16 bytes per lane
+//     issue    tile t+S-1 into slot (t-1) mod S                       (producer side)
+//     consume  read tile t from slot t mod S, apply op, store
+// so S-1 tiles are in flight while tile t is computed and stored; with S = 1
+// it is the classic load -> barrier -> compute -> barrier ("Asynchronous Data
+// Movement", opening paragraph).
 //
-// so S-1 tiles are in flight while tile t is computed and stored. With S = 1
-// the loop degenerates to the classic load -> barrier -> compute -> barrier
-// ("Asynchronous Data Movement", opening paragraph). Tiles past the end of
-// the workgroup's run are still "issued" as out-of-range loads that move no
-// data: the count of memory instructions between tile t's loads and its wait
-// is then the same for every t, and k_t is a compile-time immediate (the
-// first S-1 iterations, whose loads were issued before any store, are peeled
-// with their own smaller counts).
+// Tiles past the end of the workgroup's run are still "issued" as out-of-range
+// loads that move no data: the count of memory instructions between tile t's
+// loads and its wait is then the same for every t, and k_t is a compile-time
+// immediate (the first S-1 iterations, whose loads were issued before any
+// store, are peeled with their own smaller counts).
 //
 // Layout: a tile is tile_elems contiguous floats of global memory and sits
 // contiguously in its LDS slot. With the 16-byte path, lane `tid` moves chunk
@@ -102,7 +114,8 @@ __global__ void __launch_bounds__(256) map_kernel(MapParams p)
 
     // This workgroup's run: tiles [b T, (b + 1) T) of the input, tile j at
     // byte j * tile_bytes of the resource window [base, base + span).
-    const int64_t run_first = (int64_t)blockIdx.x * p.tiles_per_block * tile_elems;
+    const uint32_t b = blockIdx.x;
+    const int64_t run_first = (int64_t)b * p.tiles_per_block * tile_elems;
     const int64_t rem = p.n_main - run_first;
     const int64_t run_bytes = (int64_t)p.tiles_per_block * tile_bytes;
     const uint32_t span = rem <= 0 ? 0u : (uint32_t)(rem * 4 < run_bytes ? rem * 4 : run_bytes);
@@ -154,6 +167,27 @@ __global__ void __launch_bounds__(256) map_kernel(MapParams p)
 
     if (cnt == 0) {
         // only the final partial chunk (below) is left for this workgroup
+    } else if constexpr (map_wave_local(LX4, SX4)) {
+        static_for<0, S - 1>([&](auto s) TP_INLINE { issue(s, ring + s * tile_bytes); });
+        // Warm-up iterations 0 .. S-2 with their own wait counts (cnt >= 1 here,
+        // so iteration 0 always runs). Every iteration issues before it stores,
+        // so whichever iteration runs last leaves only its stores behind its
+        // final load.
+        static_for<0, S - 1>([&](auto T) TP_INLINE {
+            if ((int)T == 0 || (int)T < cnt) {
+                issue(T + S - 1, ring + ((T + S - 1) % S) * tile_bytes);
+                vm_wait<stage_wait_count(S, LD, ST, T, true)>();
+                consume(T, (T % S) * tile_bytes);
+            }
+        });
+        uint32_t cur = (S - 1) % S;  // slot of tile t
+        for (int t = S - 1; t < cnt; ++t) {
+            const uint32_t nxt = cur == 0 ? S - 1 : cur - 1;  // slot of tile t + S - 1
+            issue(t + S - 1, ring + nxt * tile_bytes);
+            vm_wait<stage_wait_count(S, LD, ST, S - 1, true)>();
+            consume(t, cur * tile_bytes);
+            cur = cur + 1 == S ? 0 : cur + 1;
+        }
     } else if constexpr (S == 1) {
         for (int t = 0; t < cnt; ++t) {
             issue(t, ring);
@@ -164,17 +198,12 @@ __global__ void __launch_bounds__(256) map_kernel(MapParams p)
         }
     } else {
         static_for<0, S - 1>([&](auto s) TP_INLINE { issue(s, ring + s * tile_bytes); });
-        bool stop = false;
         static_for<0, S - 1>([&](auto T) TP_INLINE {
-            if (!stop) {
-                if ((int)T >= cnt) {
-                    stop = true;
-                } else {
-                    vm_wait<stage_wait_count(S, LD, ST, T)>();
-                    block_sync();
-                    issue(T + S - 1, ring + ((T + S - 1) % S) * tile_bytes);
-                    consume(T, (T % S) * tile_bytes);
-                }
+            if ((int)T == 0 || (int)T < cnt) {    // cnt is uniform: every wave takes the barrier
+                vm_wait<stage_wait_count(S, LD, ST, T)>();
+                block_sync();
+                issue(T + S - 1, ring + ((T + S - 1) % S) * tile_bytes);
+                consume(T, (T % S) * tile_bytes);
             }
         });
         uint32_t cur = (S - 1) % S;  // slot of tile t
@@ -191,7 +220,7 @@ __global__ void __launch_bounds__(256) map_kernel(MapParams p)
     // The final partial 16-byte chunk (n not a multiple of 4): at most three
     // floats, moved element-wise by the first wave of the last workgroup
     // through an LDS area of its own.
-    if (p.n > p.n_main && blockIdx.x == gridDim.x - 1 && wave_first == 0) {
+    if (p.n > p.n_main && b == gridDim.x - 1 && wave_first == 0) {
         const uint32_t tail = (uint32_t)(p.n - p.n_main);
         const BufferRes ti = make_buffer_res(p.in + p.n_main, tail * 4);
         const BufferRes to = make_buffer_res(p.out + p.n_main, tail * 4);
@@ -203,7 +232,11 @@ __global__ void __launch_bounds__(256) map_kernel(MapParams p)
         store_b32(to, tid * 4, f2u(v[0]));
     }
     // No copy into LDS may still be in flight when the workgroup's LDS is freed.
-    vm_wait<0>();
+    // Every path ends with one tile's ST stores (or the tail's single store
+    // after a full wait) issued after the last load; operations retire in
+    // issue order, so at most ST outstanding means every load has landed. The
+    // final stores themselves need no wait before the program ends.
+    vm_wait<ST>();
 }
 
 // Kernel table of one op: index ((S-1) * 4 + log2 L) * 4 + path.

@@ -113,7 +113,8 @@ int plan_map(uintptr_t in, uintptr_t out, int64_t n, int op, int tile_elems, int
     const bool load_x4 = !(p.path & TP_PATH_SCALAR_LOAD);
     const bool store_x4 = !(p.path & TP_PATH_SCALAR_STORE);
     p.wait_steady = stage_wait_count(stages, map_loads_per_tile(load_x4, g.lane_chunks),
-                                     map_stores_per_tile(store_x4, g.lane_chunks), stages);
+                                     map_stores_per_tile(store_x4, g.lane_chunks), stages,
+                                     map_wave_local(load_x4, store_x4));
     const int64_t n_main = n & ~int64_t(3);
     p.num_tiles = ceil_div(n_main, tile_elems);
     p.grid = n == 0 ? 0 : (p.num_tiles == 0 ? 1 : ceil_div(p.num_tiles, tpb));

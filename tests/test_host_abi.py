@@ -89,12 +89,17 @@ def test_map_plan_paths_follow_alignment():
 
 
 def test_map_plan_wait_counts():
-    # steady-state vmcnt: (S-2) loads + (S-1) stores per lane between a tile's
-    # load and its wait; 0 for S = 1; clamped to 63
+    # steady-state vmcnt between a tile's last load and its wait, per lane:
+    # matching widths refill before waiting, (S-1) loads + (S-1) stores;
+    # mixed widths wait before the barrier and refill, (S-2) loads + (S-1) stores;
+    # 0 for S = 1; clamped to 63
     assert tp.plan_map(A, B, 100, stages=1).wait_steady == 0
-    assert tp.plan_map(A, B, 100, stages=2).wait_steady == 1
-    assert tp.plan_map(A, B, 100, stages=4, tile_elems=4096).wait_steady == 2 * 4 + 3 * 4
+    assert tp.plan_map(A, B, 100, stages=2).wait_steady == 1 + 1
+    assert tp.plan_map(A, B, 100, stages=4, tile_elems=4096).wait_steady == 3 * 4 + 3 * 4
+    assert tp.plan_map(A + 4, B + 4, 100, stages=2, tile_elems=1024).wait_steady == 4 + 4
+    assert tp.plan_map(A + 4, B, 100, stages=1, tile_elems=1024).wait_steady == 0
     assert tp.plan_map(A + 4, B, 100, stages=3, tile_elems=1024).wait_steady == 4 + 2
+    assert tp.plan_map(A, B + 4, 100, stages=2, tile_elems=2048).wait_steady == 0 + 8
     assert tp.plan_map(A + 4, B + 4, 100, stages=8, tile_elems=8192).wait_steady == 63
 
 

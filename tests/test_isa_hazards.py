@@ -12,7 +12,9 @@ code object built here and verify the rules those asm blocks must keep:
 * every 16-byte store is followed by a wait state (store-data hazard);
 * no instruction touches memory without a range check (no global_, flat_ or
   scratch_ instructions) and nothing writes through the scalar cache;
-* a kernel drains its LDS-DMA loads (vmcnt(0)) before it ends.
+* on every path through a kernel's control flow, each LDS-DMA load has
+  retired before s_endpgm (a vmcnt wait small enough that only operations
+  issued after the last such load can still be outstanding).
 """
 import os
 import re
@@ -35,8 +37,8 @@ def _sregs(tok: str):
     return {int(m.group(1))} if m else set()
 
 
-@pytest.fixture(scope="module")
-def kernels():
+def _disassemble():
+    """{kernel name: [(op, operands, address, branch target address or None)]}"""
     lib = tilepipe.library_path()
     if not os.path.exists(lib):
         pytest.skip("libtilepipe.so is not built")
@@ -52,17 +54,30 @@ def kernels():
         for obj in objs:
             out = subprocess.run([OBJDUMP, "-d", "--mcpu=gfx950", obj], check=True,
                                  capture_output=True, text=True).stdout
-            name = None
+            name = base = None
             for line in out.splitlines():
-                m = re.match(r"^[0-9a-f]+ <(.*)>:", line)
+                m = re.match(r"^([0-9a-f]+) <(.*)>:", line)
                 if m:
-                    name = m.group(1)
+                    base, name = int(m.group(1), 16), m.group(2)
                     funcs[name] = []
                     continue
-                m = re.match(r"\s+([a-z_0-9]+)\s*(.*?)\s*//", line)
+                m = re.match(r"\s+([a-z_0-9]+)\s*(.*?)\s*// ([0-9A-Fa-f]+):(.*)$", line)
                 if m and name:
-                    funcs[name].append((m.group(1), [t.strip() for t in m.group(2).split(",")]))
+                    t = re.search(r"<(.*)\+0x([0-9a-f]+)>", m.group(4))
+                    target = base + int(t.group(2), 16) if t and t.group(1) == name else None
+                    funcs[name].append((m.group(1), [x.strip() for x in m.group(2).split(",")],
+                                        int(m.group(3), 16), target))
     return funcs
+
+
+@pytest.fixture(scope="module")
+def disassembly():
+    return _disassemble()
+
+
+@pytest.fixture(scope="module")
+def kernels(disassembly):
+    return {k: [(op, ops) for op, ops, _, _ in v] for k, v in disassembly.items()}
 
 
 def test_kernels_present(kernels):
@@ -116,16 +131,92 @@ def test_no_unchecked_or_scalar_memory_writes(kernels):
                                       "s_dcache_wb", "s_dcache_discard")), (name, op)
 
 
-def test_lds_dma_drained_before_end(kernels):
-    for name, insts in kernels.items():
-        last_dma = max((i for i, (op, ops) in enumerate(insts)
-                        if op.startswith("buffer_load") and "lds" in ops[-1]), default=None)
-        if last_dma is None:
+def _is_lds_dma(op, ops):
+    return op.startswith("buffer_load") and "lds" in ops[-1]
+
+
+DRAINED = 1 << 30       # no LDS-DMA load can be outstanding
+
+
+def _undrained_end(insts):
+    """Forward dataflow over one kernel's control-flow graph. The state at an
+    instruction is the smallest number, over all paths reaching it, of
+    vector-memory operations issued since the last LDS-DMA load (DRAINED once a
+    wait has retired every such load). Vector-memory operations of a wave
+    retire in issue order, so vmcnt(k) with k not above that number retires
+    the load. Returns the index of an s_endpgm reachable with a load in
+    flight, else None; the second value counts the s_endpgm visits."""
+    index = {addr: i for i, (_, _, addr, _) in enumerate(insts)}
+    state = [None] * len(insts)
+    state[0] = DRAINED
+    work, ends = [0], 0
+    while work:
+        i = work.pop()
+        op, ops, _, target = insts[i]
+        cur = state[i]
+        assert not op.startswith(("s_setpc", "s_swappc", "s_getpc")), op
+        if _is_lds_dma(op, ops):
+            cur = 0
+        elif op.startswith("buffer_"):
+            cur = cur if cur == DRAINED else cur + 1
+        elif op == "s_waitcnt":
+            m = re.search(r"vmcnt\((\d+)\)", " ".join(ops))
+            if m and int(m.group(1)) <= cur:
+                cur = DRAINED
+        if op == "s_endpgm":
+            ends += 1
+            if cur != DRAINED:
+                return i, ends
             continue
-        ends = [i for i, (op, _) in enumerate(insts) if op == "s_endpgm"]
-        assert ends
-        for e in ends:
-            if e < last_dma:
-                continue
-            seg = insts[last_dma:e]
-            assert any(op == "s_waitcnt" and "vmcnt(0)" in " ".join(ops) for op, ops in seg), name
+        succ = []
+        if op.startswith(("s_branch", "s_cbranch")):
+            assert target is not None and target in index, (i, op)
+            succ.append(index[target])
+        if op != "s_branch" and i + 1 < len(insts):
+            succ.append(i + 1)
+        for j in succ:
+            new = cur if state[j] is None else min(state[j], cur)
+            if new != state[j]:
+                state[j] = new
+                work.append(j)
+    return None, ends
+
+
+def _seq(*items):
+    """Synthetic instruction list: items are (op, operand string[, target index])."""
+    out = []
+    for i, it in enumerate(items):
+        op, ops = it[0], [x.strip() for x in it[1].split(",")]
+        target = 4 * it[2] if len(it) > 2 else None
+        out.append((op, ops, 4 * i, target))
+    return out
+
+
+DMA = ("buffer_load_dwordx4", "v1, s[0:3], 0 offen nt lds")
+STORE = ("buffer_store_dwordx4", "v[2:5], v1, s[4:7], 0 offen sc1 nt")
+END = ("s_endpgm", "")
+
+
+def test_drain_dataflow_on_known_sequences():
+    assert _undrained_end(_seq(DMA, STORE, ("s_waitcnt", "vmcnt(1)"), END))[0] is None
+    assert _undrained_end(_seq(DMA, STORE, ("s_waitcnt", "vmcnt(2)"), END))[0] == 3
+    assert _undrained_end(_seq(DMA, ("s_waitcnt", "lgkmcnt(0)"), END))[0] == 2
+    assert _undrained_end(_seq(DMA, ("s_waitcnt", "vmcnt(0) lgkmcnt(0)"), END))[0] is None
+    # a branch around the only wait
+    assert _undrained_end(_seq(DMA, ("s_cbranch_scc1", "1", 3), ("s_waitcnt", "vmcnt(0)"),
+                               END))[0] == 3
+    # two paths: one drained fully then stores, one with a single store; vmcnt(1) covers both
+    assert _undrained_end(_seq(DMA, ("s_cbranch_scc1", "1", 5), ("s_waitcnt", "vmcnt(0)"), STORE,
+                               ("s_branch", "1", 6), STORE, ("s_waitcnt", "vmcnt(1)"), END))[0] is None
+    # a loop whose back edge re-enters after a load with no store behind it
+    assert _undrained_end(_seq(STORE, DMA, ("s_cbranch_scc1", "1", 0), ("s_waitcnt", "vmcnt(1)"),
+                               END))[0] == 4
+
+
+def test_lds_dma_drained_before_end(disassembly):
+    checked = 0
+    for name, insts in disassembly.items():
+        bad, ends = _undrained_end(insts)
+        assert bad is None, f"{name}: s_endpgm at index {bad} with an LDS-DMA load in flight"
+        checked += ends
+    assert checked > 100
