@@ -41,8 +41,9 @@ def parse():
     ap.add_argument("--tiles-per-block", type=int, default=0,
                     help="consecutive tiles per workgroup (0: the library default)")
     ap.add_argument("--quick", action="store_true", help="headline only: no sweep, no extra rows")
-    ap.add_argument("--mode", choices=("bench", "stages"), default="bench",
-                    help="stages: only run the maps at 1-4 stages (for hardware-counter passes)")
+    ap.add_argument("--mode", choices=("bench", "stages", "sweep"), default="bench",
+                    help="stages: only the maps at 1-4 stages; sweep: only the 24-point stage/tile "
+                         "sweep (both for hardware-counter passes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline")
@@ -73,6 +74,23 @@ def time_launches(fn, warmup: int, steps: int):
     torch.cuda.synchronize()
     per = [a.elapsed_time(b) for a, b in zip(starts, ends)]
     return per, r0.elapsed_time(r1)
+
+
+def gpu_warmup(fn, ms: float = 150.0):
+    """Keep the GPU busy with fn for about `ms` milliseconds. Coming out of idle
+    the clocks take some 20 ms of sustained load to ramp up; launches timed
+    before that run up to a fifth slower, whichever configuration comes first."""
+    import torch
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    reps = max(1, int(ms / max(e0.elapsed_time(e1), 1e-3)))
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
 
 
 def time_region(fn, warmup: int, steps: int) -> float:
@@ -173,10 +191,39 @@ def stages_mode(args):
     for op, n, seed in (("horner32", 1 << 27, 4), ("scale2", 1 << 28, 2)):
         x = workloads.uniform_pm1(n, seed=seed).to(dev)
         y = torch.empty_like(x)
+        gpu_warmup(lambda: tp.pipelined_map(x, y, op, 1024, 2, 16))
         for S in (1, 2, 3, 4):
             per, _ = time_launches(lambda: tp.pipelined_map(x, y, op, 1024, S, 16), 2, args.steps)
             log(f"{op} tile 1024 T16 S{S}: {median(per) * 1e3:.1f} us")
         del x, y
+    torch.cuda.synchronize()
+
+
+def sweep_points():
+    """The stage/tile sweep of scale-by-2 over 2^28 floats: source offset 0 and
+    4 bytes (misaligned fallback) x tile 256/1024/4096 x stages 1-4, at the
+    library's run length."""
+    return [(off, T, S) for off in (0, 1) for T in (256, 1024, 4096) for S in (1, 2, 3, 4)]
+
+
+def sweep_mode(args):
+    """Each sweep point `steps` times in order, for per-point counter passes
+    (a point is told apart by kernel name, grid and workgroup size)."""
+    import torch
+    import software_pipelining_amd as tp
+    from software_pipelining_amd import workloads
+    dev = torch.device("cuda:0")
+    n = 1 << 28
+    xbuf = torch.zeros(n + 4, dtype=torch.float32, device=dev)
+    xbuf[:n].copy_(workloads.uniform_pm1(n, seed=2))
+    y = torch.empty(n, dtype=torch.float32, device=dev)
+    gpu_warmup(lambda: tp.pipelined_map(xbuf[:n], y, "scale2", 256, 2, 0))
+    for off, T, S in sweep_points():
+        xin = xbuf[off:off + n]
+        plan = tp.plan_map(xin.data_ptr(), y.data_ptr(), n, "scale2", T, S, 0)
+        per, _ = time_launches(lambda: tp.pipelined_map(xin, y, "scale2", T, S, 0), 1, args.steps)
+        log(f"sweep offset {4 * off}B tile {T} S{S} grid {plan.grid} threads {plan.threads} "
+            f"path {tp.Path(plan.path).name.lower()}: {median(per) * 1e3:.1f} us")
     torch.cuda.synchronize()
 
 
@@ -189,6 +236,9 @@ def main():
 
     if args.mode == "stages":
         stages_mode(args)
+        return
+    if args.mode == "sweep":
+        sweep_mode(args)
         return
 
     import numpy as np
@@ -220,6 +270,7 @@ def main():
     parity = sampled_parity(x_host, y, "scale2")
     log(f"headline parity (sampled windows vs oracle): {parity}")
     step = lambda: tp.pipelined_map(x, y, "scale2", T, S, TPB)
+    gpu_warmup(step)
     region = time_region(step, args.warmup, args.steps)          # the whole job, back to back
     per, _ = time_launches(step, 2, args.steps)                   # per-launch kernel durations
     ms_step = region / args.steps
@@ -277,17 +328,16 @@ def extra_rows(args, tp, workloads, torch, np, dev, x_host, xbuf, y):
 
     # stage/tile sweep with the 4-byte source offset (misaligned fallback)
     sweep = []
-    for off in (0, 1):
+    gpu_warmup(lambda: tp.pipelined_map(xbuf[:n], y, "scale2", 256, 2, 0))
+    for off, T, S in sweep_points():
         xin = xbuf[off:off + n]
-        for T in (256, 1024, 4096):
-            for S in (1, 2, 3, 4):
-                p = tp.pipelined_map(xin, y, "scale2", T, S, 0)
-                per, _ = time_launches(lambda: tp.pipelined_map(xin, y, "scale2", T, S, 0), 2, 8)
-                gbs = 8 * n / (median(per) * 1e-3) / 1e9
-                sweep.append({"src_offset_bytes": 4 * off, "tile": T, "stages": S,
-                              "path": tp.Path(p).name.lower(), "GBs": round(gbs, 1),
-                              "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1)})
-        log(f"sweep offset {4 * off}B done")
+        p = tp.pipelined_map(xin, y, "scale2", T, S, 0)
+        per, _ = time_launches(lambda: tp.pipelined_map(xin, y, "scale2", T, S, 0), 2, 8)
+        gbs = 8 * n / (median(per) * 1e-3) / 1e9
+        sweep.append({"src_offset_bytes": 4 * off, "tile": T, "stages": S,
+                      "path": tp.Path(p).name.lower(), "GBs": round(gbs, 1),
+                      "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1)})
+    log("sweep done")
     # parity of the last (fallback) point
     rows["sweep_parity_offset4"] = bool(sampled_parity(torch.cat([x_host[1:], torch.zeros(1)])[:n], y,
                                                        "scale2"))
@@ -298,29 +348,61 @@ def extra_rows(args, tp, workloads, torch, np, dev, x_host, xbuf, y):
     xs_host = workloads.uniform_pm1(ns, seed=1)
     xs = xs_host.to(dev)
     ys = torch.empty_like(xs)
-    per, _ = time_launches(lambda: tp.pipelined_map(xs, ys, "scale2", 256, 2, 64), 5, 50)
-    gbs = 8 * ns / (median(per) * 1e-3) / 1e9
-    rows["scale2_small"] = {"n": ns, "tile": 256, "stages": 2, "GBs": round(gbs, 1),
-                            "note": "128 MiB footprint fits the 256 MB Infinity Cache: cache-warm"}
+    small = lambda: tp.pipelined_map(xs, ys, "scale2", 256, 2, 64)
+    gpu_warmup(small)
+    per, _ = time_launches(small, 5, 50)
+    warm = 8 * ns / (median(per) * 1e-3) / 1e9
+    # the same launch with the caches flushed first: 1 GiB written to another
+    # buffer between repetitions evicts the 128 MiB footprint from the 256 MB
+    # Infinity Cache and the L2s; only the map launch is between the events
+    s = torch.cuda.current_stream()
+    cold = []
+    for _ in range(20):
+        y.fill_(0.0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        small()
+        e1.record(s)
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    flushed = 8 * ns / (median(cold) * 1e-3) / 1e9
+    rows["scale2_small"] = {"n": ns, "tile": 256, "stages": 2, "tiles_per_block": 64,
+                            "GBs_cache_warm": round(warm, 1), "GBs_flushed": round(flushed, 1),
+                            "us_cache_warm": round(median(per) * 1e3, 2),
+                            "us_flushed": round(median(cold) * 1e3, 2),
+                            "note": "1 024 one-wave workgroups (64 tiles each): latency-bound by the "
+                                    "configuration; the 128 MiB footprint fits the Infinity Cache"}
+    log(f"scale2 small: warm {warm:.0f} GB/s, flushed {flushed:.0f} GB/s")
     del xs, ys
 
-    # compute-heavy map: 2^27, horner32, tile 1024, stages 1/2/4, at the
-    # library's run length and at 16 tiles per workgroup (fixed grid and
-    # occupancy across stages: 8 workgroups per CU either way)
+    # compute-heavy map: 2^27, horner32, stages 1/2/4
     nh = 1 << 27
     xh_host = workloads.uniform_pm1(nh, seed=4)
     xh = xh_host.to(dev)
     yh = torch.empty_like(xh)
     hr = {}
-    for tpb in (0, 16):
-        for S in (1, 2, 4):
-            tp.pipelined_map(xh, yh, "horner32", 1024, S, tpb)
-            per, _ = time_launches(lambda: tp.pipelined_map(xh, yh, "horner32", 1024, S, tpb), 3, 10)
-            t = median(per) * 1e-3
-            hr[f"T{tpb or 'default'}_S{S}"] = {"GBs": round(8 * nh / t / 1e9, 1),
-                                               "TFLOPs": round(64 * nh / t / 1e12, 2),
-                                               "us": round(t * 1e6, 1)}
-        key = f"T{tpb or 'default'}"
+    # tile 1024 (the workload's tile) at the library's run length and at 16
+    # tiles per workgroup, and tile 256 (one-wave workgroups) at the library's run
+    groups = [(1024, 0), (1024, 16), (256, 0)]
+    configs = [(tile, tpb, S) for tile, tpb in groups for S in (1, 2, 4)]
+    for tile, tpb, S in configs:
+        tp.pipelined_map(xh, yh, "horner32", tile, S, tpb)
+    gpu_warmup(lambda: tp.pipelined_map(xh, yh, "horner32", 1024, 2, 0))
+    # the configurations take turns over several rounds, so that a drift of the
+    # clocks during the run does not favour whichever ran first
+    times = {c: [] for c in configs}
+    for _ in range(6):
+        for tile, tpb, S in configs:
+            per, _ = time_launches(lambda: tp.pipelined_map(xh, yh, "horner32", tile, S, tpb), 1, 4)
+            times[(tile, tpb, S)] += per
+    name = lambda tile, tpb: ("" if tile == 1024 else f"tile{tile}_") + f"T{tpb or 'default'}"
+    for tile, tpb, S in configs:
+        t = median(times[(tile, tpb, S)]) * 1e-3
+        hr[f"{name(tile, tpb)}_S{S}"] = {"GBs": round(8 * nh / t / 1e9, 1),
+                                         "TFLOPs": round(64 * nh / t / 1e12, 2),
+                                         "us": round(t * 1e6, 1)}
+    for tile, tpb in groups:
+        key = name(tile, tpb)
         hr[f"{key}_speedup_S2_over_S1"] = round(hr[f"{key}_S1"]["us"] / hr[f"{key}_S2"]["us"], 3)
         hr[f"{key}_speedup_S4_over_S1"] = round(hr[f"{key}_S1"]["us"] / hr[f"{key}_S4"]["us"], 3)
     hr["parity"] = bool(sampled_parity(xh_host, yh, "horner32"))

@@ -147,6 +147,7 @@ def _undrained_end(insts):
     the load. Returns the index of an s_endpgm reachable with a load in
     flight, else None; the second value counts the s_endpgm visits."""
     index = {addr: i for i, (_, _, addr, _) in enumerate(insts)}
+    jumps = _long_jumps(insts)
     state = [None] * len(insts)
     state[0] = DRAINED
     work, ends = [0], 0
@@ -154,7 +155,9 @@ def _undrained_end(insts):
         i = work.pop()
         op, ops, _, target = insts[i]
         cur = state[i]
-        assert not op.startswith(("s_setpc", "s_swappc", "s_getpc")), op
+        assert not op.startswith("s_swappc"), op
+        if op.startswith(("s_setpc", "s_getpc")):
+            assert i in jumps or i + 3 in jumps, (i, op)     # only the long-jump pattern
         if _is_lds_dma(op, ops):
             cur = 0
         elif op.startswith("buffer_"):
@@ -169,6 +172,14 @@ def _undrained_end(insts):
                 return i, ends
             continue
         succ = []
+        if i in jumps:
+            assert jumps[i] in index, (i, op)
+            state_target = index[jumps[i]]
+            new = cur if state[state_target] is None else min(state[state_target], cur)
+            if new != state[state_target]:
+                state[state_target] = new
+                work.append(state_target)
+            continue
         if op.startswith(("s_branch", "s_cbranch")):
             assert target is not None and target in index, (i, op)
             succ.append(index[target])
@@ -180,6 +191,25 @@ def _undrained_end(insts):
                 state[j] = new
                 work.append(j)
     return None, ends
+
+
+def _long_jumps(insts):
+    """{index of s_setpc_b64: target address} for the assembler's long-jump
+    sequence  s_getpc_b64 s[a:b]; s_add_u32/s_sub_u32 sa, sa, imm;
+    s_addc_u32/s_subb_u32 sb, sb, 0; s_setpc_b64 s[a:b]. s_getpc_b64 yields
+    the address of the instruction after it."""
+    out = {}
+    for i, (op, ops, addr, _) in enumerate(insts):
+        if op != "s_getpc_b64" or i + 3 >= len(insts):
+            continue
+        pair = ops[0]
+        lo = "s" + pair[2:pair.index(":")]
+        (op1, ops1, _, _), (op2, _, _, _), (op3, ops3, _, _) = insts[i + 1:i + 4]
+        assert op1 in ("s_add_u32", "s_sub_u32") and ops1[0] == lo and ops1[1] == lo, (i, op1, ops1)
+        assert op2 in ("s_addc_u32", "s_subb_u32") and op3 == "s_setpc_b64" and ops3[0] == pair, (i, op2, op3)
+        imm = int(ops1[2], 0)
+        out[i + 3] = addr + 4 + (imm if op1 == "s_add_u32" else -imm)
+    return out
 
 
 def _seq(*items):
@@ -208,6 +238,13 @@ def test_drain_dataflow_on_known_sequences():
     # two paths: one drained fully then stores, one with a single store; vmcnt(1) covers both
     assert _undrained_end(_seq(DMA, ("s_cbranch_scc1", "1", 5), ("s_waitcnt", "vmcnt(0)"), STORE,
                                ("s_branch", "1", 6), STORE, ("s_waitcnt", "vmcnt(1)"), END))[0] is None
+    # a long jump over the only wait (s_getpc_b64 at byte 4 yields 8; 8 + 12 = 20 = index 5)
+    assert _undrained_end(_seq(DMA, ("s_getpc_b64", "s[0:1]"), ("s_add_u32", "s0, s0, 12"),
+                               ("s_addc_u32", "s1, s1, 0"), ("s_setpc_b64", "s[0:1]"),
+                               ("s_waitcnt", "vmcnt(0)"), END))[0] is None
+    assert _undrained_end(_seq(DMA, ("s_getpc_b64", "s[0:1]"), ("s_add_u32", "s0, s0, 16"),
+                               ("s_addc_u32", "s1, s1, 0"), ("s_setpc_b64", "s[0:1]"),
+                               ("s_waitcnt", "vmcnt(0)"), END))[0] == 6
     # a loop whose back edge re-enters after a load with no store behind it
     assert _undrained_end(_seq(STORE, DMA, ("s_cbranch_scc1", "1", 0), ("s_waitcnt", "vmcnt(1)"),
                                END))[0] == 4
