@@ -41,9 +41,10 @@ def parse():
     ap.add_argument("--tiles-per-block", type=int, default=0,
                     help="consecutive tiles per workgroup (0: the library default)")
     ap.add_argument("--quick", action="store_true", help="headline only: no sweep, no extra rows")
-    ap.add_argument("--mode", choices=("bench", "stages", "sweep"), default="bench",
+    ap.add_argument("--mode", choices=("bench", "stages", "sweep", "occupancy"), default="bench",
                     help="stages: only the maps at 1-4 stages; sweep: only the 24-point stage/tile "
-                         "sweep (both for hardware-counter passes)")
+                         "sweep (both for hardware-counter passes); occupancy: scale2 bandwidth "
+                         "against the bound on resident workgroups per CU")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline")
@@ -182,19 +183,25 @@ def cpu_baseline(x_host, op, bytes_per_elem, seconds):
 
 
 def stages_mode(args):
-    """Launch the maps at stages 1..4 with a fixed grid and occupancy (tile 1024,
-    16 tiles per workgroup), a few times each, for per-stage counter passes."""
+    """Launch the maps at stages 1..4 with a fixed grid and occupancy, a few
+    times each, for per-stage counter passes: tile 1024 with 16 tiles per
+    workgroup and no bound on resident workgroups (8 per CU, wave-limited),
+    and horner32 also with 8 tiles per workgroup at 2 workgroups per CU."""
     import torch
     import software_pipelining_amd as tp
     from software_pipelining_amd import workloads
     dev = torch.device("cuda:0")
-    for op, n, seed in (("horner32", 1 << 27, 4), ("scale2", 1 << 28, 2)):
+    for op, n, seed, runs in (("horner32", 1 << 27, 4, ((16, -1), (8, 2))),
+                              ("scale2", 1 << 28, 2, ((16, -1),))):
         x = workloads.uniform_pm1(n, seed=seed).to(dev)
         y = torch.empty_like(x)
-        gpu_warmup(lambda: tp.pipelined_map(x, y, op, 1024, 2, 16))
-        for S in (1, 2, 3, 4):
-            per, _ = time_launches(lambda: tp.pipelined_map(x, y, op, 1024, S, 16), 2, args.steps)
-            log(f"{op} tile 1024 T16 S{S}: {median(per) * 1e3:.1f} us")
+        gpu_warmup(lambda: tp.pipelined_map(x, y, op, 1024, 2, 16, resident_cap=-1))
+        for tpb, cap in runs:
+            for S in (1, 2, 3, 4):
+                f = lambda: tp.pipelined_map(x, y, op, 1024, S, tpb, resident_cap=cap)
+                per, _ = time_launches(f, 2, args.steps)
+                occ = "8 WG/CU" if cap < 0 else f"{cap} WG/CU"
+                log(f"{op} tile 1024 T{tpb} {occ} S{S}: {median(per) * 1e3:.1f} us")
         del x, y
     torch.cuda.synchronize()
 
@@ -227,6 +234,42 @@ def sweep_mode(args):
     torch.cuda.synchronize()
 
 
+def occupancy_mode(args):
+    """scale2 over 2^28 at tiles 256/1024/4096, runs of 2/4/8, 1/2/4 stages:
+    bandwidth with no bound on resident workgroups, with the library's bound,
+    and with every explicit bound, in interleaved rounds."""
+    import torch
+    import software_pipelining_amd as tp
+    dev = torch.device("cuda:0")
+    n = 1 << 28
+    x = torch.empty(n, device=dev).uniform_(-1, 1)
+    y = torch.empty_like(x)
+    gpu_warmup(lambda: tp.pipelined_map(x, y, "scale2", 256, 2, 0), 300)
+    points = []
+    for tile in (256, 1024, 4096):
+        waves = min(256, tile // 4) // 64
+        for T in (2, 4, 8):
+            for S in (1, 2, 4):
+                for cap in [-1, 0] + list(range(max(1, 8 // waves), 32 // waves)):
+                    points.append((tile, T, S, cap))
+    res = {p: [] for p in points}
+    for _ in range(2):
+        for tile, T, S, cap in points:
+            f = lambda: tp.pipelined_map(x, y, "scale2", tile, S, T, resident_cap=cap)
+            res[(tile, T, S, cap)].append(8 * n / (time_region(f, 2, args.steps) / args.steps * 1e-3) / 1e9)
+    for tile in (256, 1024, 4096):
+        for T in (2, 4, 8):
+            for S in (1, 2, 4):
+                row = {cap: round(median(v)) for (t, tt, s, cap), v in res.items()
+                       if (t, tt, s) == (tile, T, S)}
+                policy = tp.plan_map(x.data_ptr(), y.data_ptr(), n, "scale2", tile, S, T).resident_cap
+                best = max((v, c) for c, v in row.items() if c > 0)
+                log(f"occupancy tile {tile} T{T} S{S}: none {row[-1]} policy(cap {policy or '-'}) "
+                    f"{row[0]} best cap {best[1]} {best[0]} | " +
+                    " ".join(f"{c}:{v}" for c, v in row.items() if c > 0))
+    torch.cuda.synchronize()
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -239,6 +282,9 @@ def main():
         return
     if args.mode == "sweep":
         sweep_mode(args)
+        return
+    if args.mode == "occupancy":
+        occupancy_mode(args)
         return
 
     import numpy as np
@@ -297,7 +343,9 @@ def main():
                                f"uniform [-1,1) seed 2, tile {T} fp32, {S} stages, "
                                f"{plan.tiles_per_block} tiles per workgroup, 16-byte path",
                    "n": n, "tile_elems": T, "stages": S, "tiles_per_block": plan.tiles_per_block,
-                   "grid": plan.grid, "path": tp.Path(path).name.lower()},
+                   "grid": plan.grid, "path": tp.Path(path).name.lower(),
+                   "resident_workgroups_per_cu": plan.resident_cap or None,
+                   "lds_bytes_per_workgroup": plan.lds_bytes},
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "parity": "bit-exact on sampled windows" if parity else "MISMATCH",
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
@@ -381,28 +429,34 @@ def extra_rows(args, tp, workloads, torch, np, dev, x_host, xbuf, y):
     xh = xh_host.to(dev)
     yh = torch.empty_like(xh)
     hr = {}
+    # (tile, tiles per workgroup, bound on resident workgroups per CU):
     # tile 1024 (the workload's tile) at the library's run length and at 16
-    # tiles per workgroup, and tile 256 (one-wave workgroups) at the library's run
-    groups = [(1024, 0), (1024, 16), (256, 0)]
-    configs = [(tile, tpb, S) for tile, tpb in groups for S in (1, 2, 4)]
-    for tile, tpb, S in configs:
-        tp.pipelined_map(xh, yh, "horner32", tile, S, tpb)
-    gpu_warmup(lambda: tp.pipelined_map(xh, yh, "horner32", 1024, 2, 0))
+    # tiles per workgroup, tile 256 (one-wave workgroups) at the library's run,
+    # and tile 1024 with 8 tiles per workgroup at 2 workgroups (8 waves) per CU,
+    # the occupancy of a kernel whose registers or LDS leave few waves resident
+    groups = [(1024, 0, 0), (1024, 16, 0), (256, 0, 0), (1024, 8, 2)]
+    configs = [(tile, tpb, cap, S) for tile, tpb, cap in groups for S in (1, 2, 4)]
+    run = lambda tile, tpb, cap, S: tp.pipelined_map(xh, yh, "horner32", tile, S, tpb,
+                                                     resident_cap=cap)
+    for c in configs:
+        run(*c)
+    gpu_warmup(lambda: run(1024, 0, 0, 2))
     # the configurations take turns over several rounds, so that a drift of the
     # clocks during the run does not favour whichever ran first
     times = {c: [] for c in configs}
     for _ in range(6):
-        for tile, tpb, S in configs:
-            per, _ = time_launches(lambda: tp.pipelined_map(xh, yh, "horner32", tile, S, tpb), 1, 4)
-            times[(tile, tpb, S)] += per
-    name = lambda tile, tpb: ("" if tile == 1024 else f"tile{tile}_") + f"T{tpb or 'default'}"
-    for tile, tpb, S in configs:
-        t = median(times[(tile, tpb, S)]) * 1e-3
-        hr[f"{name(tile, tpb)}_S{S}"] = {"GBs": round(8 * nh / t / 1e9, 1),
-                                         "TFLOPs": round(64 * nh / t / 1e12, 2),
-                                         "us": round(t * 1e6, 1)}
-    for tile, tpb in groups:
-        key = name(tile, tpb)
+        for c in configs:
+            per, _ = time_launches(lambda: run(*c), 1, 4)
+            times[c] += per
+    name = lambda tile, tpb, cap: (("" if tile == 1024 else f"tile{tile}_") + f"T{tpb or 'default'}"
+                                   + (f"_{cap}wg_per_cu" if cap else ""))
+    for tile, tpb, cap, S in configs:
+        t = median(times[(tile, tpb, cap, S)]) * 1e-3
+        hr[f"{name(tile, tpb, cap)}_S{S}"] = {"GBs": round(8 * nh / t / 1e9, 1),
+                                              "TFLOPs": round(64 * nh / t / 1e12, 2),
+                                              "us": round(t * 1e6, 1)}
+    for tile, tpb, cap in groups:
+        key = name(tile, tpb, cap)
         hr[f"{key}_speedup_S2_over_S1"] = round(hr[f"{key}_S1"]["us"] / hr[f"{key}_S2"]["us"], 3)
         hr[f"{key}_speedup_S4_over_S1"] = round(hr[f"{key}_S1"]["us"] / hr[f"{key}_S4"]["us"], 3)
     hr["parity"] = bool(sampled_parity(xh_host, yh, "horner32"))

@@ -85,6 +85,9 @@ typedef struct tp_plan {
     int32_t wait_steady;     /* vmcnt immediate of the steady-state stage wait */
     int64_t num_tiles;       /* tiles over the whole problem */
     int64_t grid;            /* workgroups launched (0: nothing to launch) */
+    int32_t ring_bytes;      /* LDS the kernel itself needs (the ring and its tail area) */
+    int32_t resident_cap;    /* about this many workgroups per CU (0: hardware limits only);
+                                lds_bytes is padded up to bound residency */
 } tp_plan;
 
 /* Human-readable name of a tp_status value ("TP_OK", ...); never NULL. */
@@ -143,6 +146,32 @@ TP_API int tp_pipelined_map(const float *in, float *out, int64_t n, int op,
                             void *stream, int *path_out);
 
 /*
+ * tp_pipelined_map with an explicit bound on resident workgroups per CU
+ * (tp_pipelined_map is this call with resident_cap 0). The bound is applied by
+ * reserving LDS: each workgroup is given floor(160 KiB / cap) rounded down to
+ * whole KiB (so about cap workgroups fit on a CU, a few more where the
+ * rounding leaves room), or the ring's own size if that is larger, and never
+ * more than the device's LDS per workgroup. It changes how much tile traffic
+ * is in flight at once on a CU, never the result.
+ *   resident_cap  0: the library's policy. For the streaming ops (scale2,
+ *                    copy) with runs of 2 or more tiles of at most 1024
+ *                    floats it keeps about 28 KiB x (1 + 1/T) of tile traffic
+ *                    per CU in flight: each resident workgroup has a(T,S) + 1
+ *                    tiles moving on average (a = mean over a run of
+ *                    min(S, tiles left) loads, plus the stores behind them),
+ *                    with at least 4 workgroups and 8 waves resident per CU.
+ *                    horner32, runs of one tile and larger tiles (several
+ *                    loads per lane per tile) are not bounded.
+ *               -1: no bound (hardware limits only);
+ *              k>0: at most k workgroups per CU;
+ *          below -1: TP_ERR_INVALID_ARG.
+ * The other arguments, errors and results are those of tp_pipelined_map.
+ */
+TP_API int tp_pipelined_map_ex(const float *in, float *out, int64_t n, int op,
+                               int tile_elems, int stages, int tiles_per_block,
+                               int resident_cap, void *stream, int *path_out);
+
+/*
  * Predicated 16-byte chunk copy ("Asynchronous Copies", section "A
  * Global-to-Shared Copy", the paragraph on pred, src_size and ignore_src).
  * For each chunk i < n_chunks:
@@ -174,7 +203,7 @@ TP_API int tp_plan_row_shift(const void *a, const void *b, int64_t rows,
                              int64_t lds_budget, tp_plan *plan);
 TP_API int tp_plan_pipelined_map(const void *in, const void *out, int64_t n, int op,
                                  int tile_elems, int stages, int tiles_per_block,
-                                 int64_t lds_budget, tp_plan *plan);
+                                 int resident_cap, int64_t lds_budget, tp_plan *plan);
 TP_API int tp_plan_chunk_copy(const void *src, const void *dst, int64_t n_chunks,
                               const void *pred, const void *src_size,
                               const void *ignore_src, int stages, int tiles_per_block,

@@ -125,10 +125,10 @@ TP_API int tp_plan_row_shift(const void *a, const void *b, int64_t rows, int64_t
 
 TP_API int tp_plan_pipelined_map(const void *in, const void *out, int64_t n, int op,
                                  int tile_elems, int stages, int tiles_per_block,
-                                 int64_t lds_budget, tp_plan *plan)
+                                 int resident_cap, int64_t lds_budget, tp_plan *plan)
 {
     return tp::plan_map((uintptr_t)in, (uintptr_t)out, n, op, tile_elems, stages, tiles_per_block,
-                        lds_budget, plan);
+                        resident_cap, lds_budget, plan);
 }
 
 TP_API int tp_plan_chunk_copy(const void *src, const void *dst, int64_t n_chunks,
@@ -162,9 +162,17 @@ TP_API int tp_row_shift(const float *a, float *b, int64_t rows, void *stream, in
 TP_API int tp_pipelined_map(const float *in, float *out, int64_t n, int op, int tile_elems,
                             int stages, int tiles_per_block, void *stream, int *path_out)
 {
+    return tp_pipelined_map_ex(in, out, n, op, tile_elems, stages, tiles_per_block, 0, stream,
+                               path_out);
+}
+
+TP_API int tp_pipelined_map_ex(const float *in, float *out, int64_t n, int op, int tile_elems,
+                               int stages, int tiles_per_block, int resident_cap, void *stream,
+                               int *path_out)
+{
     tp_plan plan;
     int st = tp::plan_map((uintptr_t)in, (uintptr_t)out, n, op, tile_elems, stages,
-                          tiles_per_block, kNoBudget, &plan);
+                          tiles_per_block, resident_cap, kNoBudget, &plan);
     if (st != TP_OK)
         return st;
     if (path_out)
@@ -174,8 +182,12 @@ TP_API int tp_pipelined_map(const float *in, float *out, int64_t n, int op, int 
     int64_t lds = 0;
     if ((st = current_device(&lds)) != TP_OK)
         return st;
-    if (plan.lds_bytes > lds)
-        return TP_ERR_LDS_BUDGET;
+    // again with the device's budget: the ring must fit, and the LDS reserved
+    // to bound residency never exceeds it
+    st = tp::plan_map((uintptr_t)in, (uintptr_t)out, n, op, tile_elems, stages, tiles_per_block,
+                      resident_cap, lds, &plan);
+    if (st != TP_OK)
+        return st;
     tp::MapParams p;
     memset(&p, 0, sizeof p);
     p.in = in;

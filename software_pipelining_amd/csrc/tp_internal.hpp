@@ -26,6 +26,12 @@ constexpr int kVmcntMax = 63;              // vmcnt is a 6-bit counter on gfx9-f
 constexpr int64_t kMaxMapElems = int64_t(1) << 40;
 constexpr int64_t kMaxChunks = int64_t(1) << 36;
 constexpr int64_t kMaxRunBytes = int64_t(1) << 30;   // bytes one workgroup streams
+constexpr int kLdsPerCu = 160 * 1024;      // gfx950: LDS of one CU, all of it usable by one workgroup
+constexpr int kMaxWavesPerCu = 32;         // gfx950: 8 wave slots on each of 4 SIMDs
+constexpr int kLdsReserveGranule = 1024;   // padding to bound residency is whole KiB
+constexpr int kInflightTargetBytes = 28 * 1024;   // streaming map: tile traffic in flight per CU
+constexpr int kMinResidentWaves = 8;       // ... but never fewer resident waves per CU
+constexpr int kMinResidentWorkgroups = 4;  // ... nor fewer resident workgroups
 
 // Memory instructions each lane issues per tile of a pipelined loop.
 //   ld: loads per tile (LDS-DMA loads, plus metadata loads for the chunk copy)
@@ -143,7 +149,9 @@ struct RowShiftParams {
 // Pure host code (no HIP): argument validation and launch geometry.
 int plan_row_shift(uintptr_t a, uintptr_t b, int64_t rows, int64_t lds_budget, tp_plan *plan);
 int plan_map(uintptr_t in, uintptr_t out, int64_t n, int op, int tile_elems, int stages,
-             int tiles_per_block, int64_t lds_budget, tp_plan *plan);
+             int tiles_per_block, int resident_cap, int64_t lds_budget, tp_plan *plan);
+// The library's residency bound for a map launch (0: none); see tp_pipelined_map_ex.
+int map_policy_resident_cap(int op, int tile_elems, int stages, int tiles_per_block);
 int plan_chunk_copy(uintptr_t src, uintptr_t dst, int64_t n_chunks, uintptr_t pred,
                     uintptr_t src_size, uintptr_t ignore_src, int stages, int tiles_per_block,
                     int64_t lds_budget, tp_plan *plan);

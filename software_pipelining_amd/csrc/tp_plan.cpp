@@ -40,7 +40,51 @@ int resolve_tiles_per_block(int tiles_per_block, int default_value)
     return tiles_per_block;
 }
 
+// Mean number of a run's tiles loading at a wave's stage waits: at the wait
+// of iteration t, tiles t .. min(t+S-1, T-1) are in flight (refill-first
+// order; loads past the run's end move nothing).
+double mean_tiles_in_flight(int64_t T, int64_t S)
+{
+    const int64_t sum = T <= S ? T * (T + 1) / 2 : S * (S + 1) / 2 + (T - S) * S;
+    return (double)sum / (double)T;
+}
+
+// LDS a workgroup reserves so that at most `cap` workgroups fit on a CU.
+int32_t reserve_for_cap(int32_t ring_bytes, int cap, int64_t lds_budget)
+{
+    int64_t pad = (int64_t)kLdsPerCu / cap / kLdsReserveGranule * kLdsReserveGranule;
+    if (pad > lds_budget)
+        pad = lds_budget;
+    return pad > ring_bytes ? (int32_t)pad : ring_bytes;
+}
+
 }  // namespace
+
+int map_policy_resident_cap(int op, int tile_elems, int stages, int tiles_per_block)
+{
+    // A wave of the streaming ops is almost always waiting on memory, so the
+    // resident workgroups decide how much traffic is in flight; past roughly
+    // 28 KiB per CU (with headroom for the start and end of short runs) the
+    // extra requests only queue, and HBM efficiency drops. horner32 spends
+    // most of a wave's time in FMAs and needs every wave to hide it; a run of
+    // one tile has no pipeline and lives too briefly to be bounded; and where
+    // a lane moves several 16-byte chunks per tile (tiles of 2048 floats and
+    // more) its wave already keeps several loads in flight, and bounding the
+    // workgroups was measured to cost bandwidth instead.
+    const MapGeometry g = map_geometry(tile_elems);
+    if (op == TP_OP_HORNER32 || tiles_per_block <= 1 || g.lane_chunks > 1)
+        return 0;
+    const int waves = g.threads / 64;
+    const double moving = mean_tiles_in_flight(tiles_per_block, stages) + 1.0;   // loads + stores
+    const double target = kInflightTargetBytes * (1.0 + 1.0 / tiles_per_block);
+    int cap = (int)(target / (moving * tile_elems * 4.0) + 0.5);
+    int floor_wgs = (kMinResidentWaves + waves - 1) / waves;
+    if (floor_wgs < kMinResidentWorkgroups)
+        floor_wgs = kMinResidentWorkgroups;
+    if (cap < floor_wgs)
+        cap = floor_wgs;
+    return cap >= kMaxWavesPerCu / waves ? 0 : cap;
+}
 
 int plan_row_shift(uintptr_t a, uintptr_t b, int64_t rows, int64_t lds_budget, tp_plan *plan)
 {
@@ -62,6 +106,7 @@ int plan_row_shift(uintptr_t a, uintptr_t b, int64_t rows, int64_t lds_budget, t
             return TP_ERR_OVERLAP;
         p.threads = (int32_t)(ceil_div(rows, 64) * 64);
         p.lds_bytes = p.threads * 16;
+        p.ring_bytes = p.lds_bytes;
         if (p.lds_bytes > lds_budget)
             return TP_ERR_LDS_BUDGET;
         p.path = path_bits(a, b);
@@ -74,8 +119,10 @@ int plan_row_shift(uintptr_t a, uintptr_t b, int64_t rows, int64_t lds_budget, t
 }
 
 int plan_map(uintptr_t in, uintptr_t out, int64_t n, int op, int tile_elems, int stages,
-             int tiles_per_block, int64_t lds_budget, tp_plan *plan)
+             int tiles_per_block, int resident_cap, int64_t lds_budget, tp_plan *plan)
 {
+    if (resident_cap < -1)
+        return TP_ERR_INVALID_ARG;
     if (n < 0 || n > kMaxMapElems)
         return TP_ERR_INVALID_ARG;
     if (op != TP_OP_SCALE2 && op != TP_OP_HORNER32 && op != TP_OP_COPY)
@@ -97,7 +144,7 @@ int plan_map(uintptr_t in, uintptr_t out, int64_t n, int op, int tile_elems, int
     p.threads = g.threads;
     p.lane_chunks = g.lane_chunks;
     p.tiles_per_block = tpb;
-    p.lds_bytes = stages * tile_elems * 4 + kMapTailLdsBytes;
+    p.ring_bytes = stages * tile_elems * 4 + kMapTailLdsBytes;
     if (n > 0) {
         if (!in || !out)
             return TP_ERR_INVALID_ARG;
@@ -107,8 +154,13 @@ int plan_map(uintptr_t in, uintptr_t out, int64_t n, int op, int tile_elems, int
         if (in != out && overlaps(in, bytes, out, bytes))
             return TP_ERR_OVERLAP;
     }
-    if (p.lds_bytes > lds_budget)
+    if (p.ring_bytes > lds_budget)
         return TP_ERR_LDS_BUDGET;
+    const int cap = resident_cap == 0 ? map_policy_resident_cap(op, tile_elems, stages, tpb)
+                                      : resident_cap;
+    p.resident_cap = cap >= kMaxWavesPerCu / (g.threads / 64) ? 0 : (cap < 0 ? 0 : cap);
+    p.lds_bytes = p.resident_cap ? reserve_for_cap(p.ring_bytes, p.resident_cap, lds_budget)
+                                 : p.ring_bytes;
     p.path = n > 0 ? path_bits(in, out) : TP_PATH_X4;
     const bool load_x4 = !(p.path & TP_PATH_SCALAR_LOAD);
     const bool store_x4 = !(p.path & TP_PATH_SCALAR_STORE);
@@ -144,6 +196,7 @@ int plan_chunk_copy(uintptr_t src, uintptr_t dst, int64_t n_chunks, uintptr_t pr
     p.lane_chunks = 1;
     p.tiles_per_block = tpb;
     p.lds_bytes = chunk_lds_bytes(stages);
+    p.ring_bytes = p.lds_bytes;
     if (n_chunks > 0) {
         if (!src || !dst)
             return TP_ERR_INVALID_ARG;

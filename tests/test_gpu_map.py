@@ -32,7 +32,7 @@ def _run_case(dev, op, x_host, expected, in_off, out_off, tile, stages, tpb, bud
     x = to_device(x_host, dev, offset_words=in_off)
     y = out_buffer(n, torch.float32, dev, offset_words=out_off)
     plan = tp.plan_map(x.tensor.data_ptr(), y.tensor.data_ptr(), n, op, tile, stages, tpb)
-    if plan.lds_bytes > budget and n > 0:      # an empty call launches nothing, so it succeeds
+    if plan.ring_bytes > budget and n > 0:     # an empty call launches nothing, so it succeeds
         with pytest.raises(tp.TilepipeError) as e:
             tp.pipelined_map(x.tensor, y.tensor, op, tile, stages, tpb)
         assert e.value.status == 3
@@ -115,7 +115,7 @@ def test_map_results_identical_across_parameters(cuda_device):
                     x = to_device(x_host, cuda_device, offset_words=in_off)
                     y = out_buffer(n, torch.float32, cuda_device, offset_words=out_off)
                     if tp.plan_map(x.tensor.data_ptr(), y.tensor.data_ptr(), n, "horner32", tile,
-                                   stages, tpb).lds_bytes > budget:
+                                   stages, tpb).ring_bytes > budget:
                         continue
                     tp.pipelined_map(x.tensor, y.tensor, "horner32", tile, stages, tpb)
                     got = y.tensor.cpu()
@@ -123,6 +123,23 @@ def test_map_results_identical_across_parameters(cuda_device):
                         ref = got
                     assert torch.equal(got.view(torch.int32), ref.view(torch.int32))
     assert_bits_equal(ref, oracle.pipelined_map(x_host.numpy(), "horner32"), "horner32")
+
+
+@pytest.mark.parametrize("op", OPS)
+def test_map_residency_bound_keeps_results(cuda_device, op):
+    # the LDS reserved to bound residency changes scheduling only
+    n = 7 * 4096 * 3 + 5
+    x_host = workloads.uniform_pm1(n, seed=55)
+    expected = oracle.pipelined_map(x_host.numpy(), op)
+    for tile, stages, tpb in ((256, 2, 2), (1024, 4, 3), (4096, 2, 1)):
+        for cap in (-1, 0, 1, 2, 3, 17, 40):
+            for in_off, out_off in ((0, 0), (1, 0)):
+                x = to_device(x_host, cuda_device, offset_words=in_off)
+                y = out_buffer(n, torch.float32, cuda_device, offset_words=out_off)
+                tp.pipelined_map(x.tensor, y.tensor, op, tile, stages, tpb, resident_cap=cap)
+                what = f"{op} tile={tile} S={stages} T={tpb} cap={cap} in_off={in_off}"
+                assert_bits_equal(y.tensor, expected, what, nan_free=False)
+                assert y.guards_intact() and x.guards_intact(), what
 
 
 def test_map_errors(cuda_device):
@@ -136,3 +153,6 @@ def test_map_errors(cuda_device):
     with pytest.raises(tp.TilepipeError) as e:
         tp.pipelined_map(x, torch.empty_like(x), "scale2", 8192, 8)    # 256 KiB of LDS
     assert e.value.status == 3
+    with pytest.raises(tp.TilepipeError) as e:
+        tp.pipelined_map(x, torch.empty_like(x), "scale2", 1024, 2, resident_cap=-2)
+    assert e.value.status == 1

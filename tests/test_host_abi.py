@@ -56,7 +56,8 @@ def test_map_plan_geometry_runs():
         assert (p.threads, p.lane_chunks, p.tiles_per_block) == (threads, lanes, 64)
         assert p.num_tiles == (1 << 20) // tile
         assert p.grid == -(-p.num_tiles // 64)
-        assert p.lds_bytes == 2 * tile * 4 + 256
+        assert p.ring_bytes == 2 * tile * 4 + 256
+        assert p.lds_bytes >= p.ring_bytes
         assert p.path == tp.Path.X4
 
 
@@ -134,8 +135,82 @@ def test_map_plan_option_errors():
 
 def test_map_plan_lds_budget():
     assert _status(tp.plan_map, A, B, 10, "scale2", 4096, 4, 0, 64 * 1024) == 3
-    assert tp.plan_map(A, B, 10, "scale2", 4096, 4, 0, 160 * 1024).lds_bytes == 4 * 16384 + 256
+    assert tp.plan_map(A, B, 10, "scale2", 4096, 4, 0, 160 * 1024).ring_bytes == 4 * 16384 + 256
+    assert tp.plan_map(A, B, 10, "horner32", 4096, 4, 0, 160 * 1024).lds_bytes == 4 * 16384 + 256
     assert _status(tp.plan_map, A, B, 10, "scale2", 8192, 8, 0, 160 * 1024) == 3
+
+
+KIB = 1024
+
+
+def _reserve(cap, ring, budget=160 * KIB):
+    return max(ring, min(budget, (160 * KIB // cap) // KIB * KIB))
+
+
+def test_map_residency_policy_values():
+    # worked by hand from the rule: cap = round(28 KiB (1 + 1/T) / ((a + 1) tile bytes)),
+    # a = mean over the run of min(S, tiles left), at least 4 workgroups and 8 waves
+    cases = [  # tile, S, T, cap
+        (256, 2, 2, 17),     # a = 1.5: 43008 / (2.5 * 1024) = 16.8
+        (256, 1, 2, 21),     # a = 1: 43008 / 2048 = 21
+        (256, 4, 8, 8),      # a = 26/8: 32256 / (4.25 * 1024) = 7.4 -> 7, raised to 8 waves
+        (1024, 2, 2, 4),     # 43008 / (2.5 * 4096) = 4.2
+        (1024, 4, 8, 4),     # 32256 / (4.25 * 4096) = 1.9, raised to 4 workgroups
+        (512, 4, 4, 5),      # a = 2.5: 35840 / (3.5 * 2048) = 5.0
+        (2048, 2, 2, 0),     # two 16-byte loads per lane per tile: not bounded
+        (4096, 4, 2, 0),
+    ]
+    for tile, S, T, cap in cases:
+        p = tp.plan_map(A, B, 1 << 26, "scale2", tile, S, T)
+        assert p.resident_cap == cap, (tile, S, T, p.resident_cap)
+        assert p.lds_bytes == (_reserve(cap, p.ring_bytes) if cap else p.ring_bytes)
+        assert tp.plan_map(A, B, 1 << 26, "copy", tile, S, T).resident_cap == cap
+
+
+def test_map_residency_policy_rules():
+    for tile in (256, 1024, 4096):
+        for S in (1, 2, 4):
+            for T in (1, 2, 16):
+                h = tp.plan_map(A, B, 1 << 26, "horner32", tile, S, T)
+                assert (h.resident_cap, h.lds_bytes) == (0, h.ring_bytes)   # compute-heavy: none
+                p = tp.plan_map(A, B, 1 << 26, "scale2", tile, S, T)
+                if T == 1:
+                    assert p.resident_cap == 0                       # no pipeline to bound
+                waves = p.threads // 64
+                if tile > 1024:
+                    assert p.resident_cap == 0
+                if p.resident_cap:
+                    assert p.resident_cap * waves >= 8 and p.resident_cap >= 4
+                    assert p.resident_cap < 32 // waves              # below the hardware limit
+                    assert p.lds_bytes == _reserve(p.resident_cap, p.ring_bytes)
+                    assert 160 * KIB // p.lds_bytes >= p.resident_cap
+                else:
+                    assert p.lds_bytes == p.ring_bytes
+    # deeper pipelines and bigger tiles never get more resident workgroups
+    for T in (2, 4, 16):
+        caps = [tp.plan_map(A, B, 1 << 26, "scale2", 256, S, T).resident_cap or 32 for S in (1, 2, 3, 4)]
+        assert caps == sorted(caps, reverse=True), (T, caps)
+        caps = [tp.plan_map(A, B, 1 << 26, "scale2", t, 2, T).resident_cap or 32 // max(1, t // 256)
+                for t in (256, 512, 1024, 2048)]
+        assert caps == sorted(caps, reverse=True), (T, caps)
+
+
+def test_map_explicit_residency():
+    ring = 2 * 1024 * 4 + 256
+    p = tp.plan_map(A, B, 1 << 20, "scale2", 1024, 2, 2, resident_cap=-1)
+    assert (p.resident_cap, p.lds_bytes) == (0, ring)
+    for cap in (1, 2, 3, 5, 7):
+        p = tp.plan_map(A, B, 1 << 20, "horner32", 1024, 2, 2, resident_cap=cap)
+        assert (p.resident_cap, p.lds_bytes) == (cap, _reserve(cap, ring))
+    # at or above the hardware's own limit (8 workgroups of 4 waves): nothing to reserve
+    p = tp.plan_map(A, B, 1 << 20, "scale2", 1024, 2, 2, resident_cap=8)
+    assert (p.resident_cap, p.lds_bytes) == (0, ring)
+    # the reservation never exceeds the budget, and the ring still decides the error
+    p = tp.plan_map(A, B, 1 << 20, "scale2", 1024, 2, 2, 32 * KIB, resident_cap=1)
+    assert p.lds_bytes == 32 * KIB
+    p = tp.plan_map(A, B, 1 << 20, "scale2", 4096, 8, 2, resident_cap=2)     # ring > 80 KiB
+    assert p.lds_bytes == 8 * 16384 + 256
+    assert _status(tp.plan_map, A, B, 10, "scale2", 1024, 2, 2, tilepipe._NO_BUDGET, -2) == 1
 
 
 # ------------------------------------------------------------ row shift
