@@ -434,13 +434,16 @@ def extra_rows(args, tp, workloads, torch, np, dev, x_host, xbuf, y):
     # tiles per workgroup, tile 256 (one-wave workgroups) at the library's run,
     # and tile 1024 with 8 tiles per workgroup at 2 workgroups (8 waves) per CU,
     # the occupancy of a kernel whose registers or LDS leave few waves resident
-    groups = [(1024, 0, 0), (1024, 16, 0), (256, 0, 0), (1024, 8, 2)]
-    configs = [(tile, tpb, cap, S) for tile, tpb, cap in groups for S in (1, 2, 4)]
-    run = lambda tile, tpb, cap, S: tp.pipelined_map(xh, yh, "horner32", tile, S, tpb,
-                                                     resident_cap=cap)
+    # ... each with every wave loading its own part (uniform), and the first
+    # and last also with one wave doing all loads for the others (role split)
+    groups = [(1024, 0, 0, "uniform"), (1024, 16, 0, "uniform"), (256, 0, 0, "uniform"),
+              (1024, 8, 2, "uniform"), (1024, 0, 0, "role_split"), (1024, 8, 2, "role_split")]
+    configs = [(tile, tpb, cap, sched, S) for tile, tpb, cap, sched in groups for S in (1, 2, 4)]
+    run = lambda tile, tpb, cap, sched, S: tp.pipelined_map(xh, yh, "horner32", tile, S, tpb,
+                                                            resident_cap=cap, schedule=sched)
     for c in configs:
         run(*c)
-    gpu_warmup(lambda: run(1024, 0, 0, 2))
+    gpu_warmup(lambda: run(1024, 0, 0, "uniform", 2))
     # the configurations take turns over several rounds, so that a drift of the
     # clocks during the run does not favour whichever ran first
     times = {c: [] for c in configs}
@@ -448,15 +451,17 @@ def extra_rows(args, tp, workloads, torch, np, dev, x_host, xbuf, y):
         for c in configs:
             per, _ = time_launches(lambda: run(*c), 1, 4)
             times[c] += per
-    name = lambda tile, tpb, cap: (("" if tile == 1024 else f"tile{tile}_") + f"T{tpb or 'default'}"
-                                   + (f"_{cap}wg_per_cu" if cap else ""))
-    for tile, tpb, cap, S in configs:
-        t = median(times[(tile, tpb, cap, S)]) * 1e-3
-        hr[f"{name(tile, tpb, cap)}_S{S}"] = {"GBs": round(8 * nh / t / 1e9, 1),
-                                              "TFLOPs": round(64 * nh / t / 1e12, 2),
-                                              "us": round(t * 1e6, 1)}
-    for tile, tpb, cap in groups:
-        key = name(tile, tpb, cap)
+    name = lambda tile, tpb, cap, sched: (("" if tile == 1024 else f"tile{tile}_")
+                                          + f"T{tpb or 'default'}"
+                                          + (f"_{cap}wg_per_cu" if cap else "")
+                                          + ("_role_split" if sched == "role_split" else ""))
+    for tile, tpb, cap, sched, S in configs:
+        t = median(times[(tile, tpb, cap, sched, S)]) * 1e-3
+        hr[f"{name(tile, tpb, cap, sched)}_S{S}"] = {"GBs": round(8 * nh / t / 1e9, 1),
+                                                     "TFLOPs": round(64 * nh / t / 1e12, 2),
+                                                     "us": round(t * 1e6, 1)}
+    for tile, tpb, cap, sched in groups:
+        key = name(tile, tpb, cap, sched)
         hr[f"{key}_speedup_S2_over_S1"] = round(hr[f"{key}_S1"]["us"] / hr[f"{key}_S2"]["us"], 3)
         hr[f"{key}_speedup_S4_over_S1"] = round(hr[f"{key}_S1"]["us"] / hr[f"{key}_S4"]["us"], 3)
     hr["parity"] = bool(sampled_parity(xh_host, yh, "horner32"))

@@ -73,6 +73,13 @@ typedef enum tp_path {
     TP_PATH_SCALAR = 3
 } tp_path;
 
+/* How the waves of a map workgroup share the work ("Asynchronous Data
+ * Movement", section "Barriers and pipelines": producer and consumer roles). */
+typedef enum tp_schedule {
+    TP_SCHED_UNIFORM = 0,    /* every wave loads, computes and stores its own part of each tile */
+    TP_SCHED_ROLE_SPLIT = 1  /* one extra wave issues all loads; the others compute and store */
+} tp_schedule;
+
 /* Launch plan of one call: what the entry point would enqueue (host-only). */
 typedef struct tp_plan {
     int32_t path;            /* tp_path */
@@ -88,6 +95,7 @@ typedef struct tp_plan {
     int32_t ring_bytes;      /* LDS the kernel itself needs (the ring and its tail area) */
     int32_t resident_cap;    /* about this many workgroups per CU (0: hardware limits only);
                                 lds_bytes is padded up to bound residency */
+    int32_t schedule;        /* tp_schedule (map); 0 for the other entry points */
 } tp_plan;
 
 /* Human-readable name of a tp_status value ("TP_OK", ...); never NULL. */
@@ -165,11 +173,17 @@ TP_API int tp_pipelined_map(const float *in, float *out, int64_t n, int op,
  *               -1: no bound (hardware limits only);
  *              k>0: at most k workgroups per CU;
  *          below -1: TP_ERR_INVALID_ARG.
+ * schedule: TP_SCHED_UNIFORM (what tp_pipelined_map runs), or
+ * TP_SCHED_ROLE_SPLIT: the workgroup gets one more wave, which issues every
+ * load of every tile and waits for them; the other waves only read tiles from
+ * LDS, compute and store. One workgroup barrier per iteration publishes the
+ * landed tile and frees the slot the loading wave refills next (two per
+ * iteration with one stage). Other values: TP_ERR_INVALID_ARG.
  * The other arguments, errors and results are those of tp_pipelined_map.
  */
 TP_API int tp_pipelined_map_ex(const float *in, float *out, int64_t n, int op,
                                int tile_elems, int stages, int tiles_per_block,
-                               int resident_cap, void *stream, int *path_out);
+                               int resident_cap, int schedule, void *stream, int *path_out);
 
 /*
  * Predicated 16-byte chunk copy ("Asynchronous Copies", section "A
@@ -203,7 +217,8 @@ TP_API int tp_plan_row_shift(const void *a, const void *b, int64_t rows,
                              int64_t lds_budget, tp_plan *plan);
 TP_API int tp_plan_pipelined_map(const void *in, const void *out, int64_t n, int op,
                                  int tile_elems, int stages, int tiles_per_block,
-                                 int resident_cap, int64_t lds_budget, tp_plan *plan);
+                                 int resident_cap, int schedule, int64_t lds_budget,
+                                 tp_plan *plan);
 TP_API int tp_plan_chunk_copy(const void *src, const void *dst, int64_t n_chunks,
                               const void *pred, const void *src_size,
                               const void *ignore_src, int stages, int tiles_per_block,

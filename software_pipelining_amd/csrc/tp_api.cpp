@@ -125,10 +125,11 @@ TP_API int tp_plan_row_shift(const void *a, const void *b, int64_t rows, int64_t
 
 TP_API int tp_plan_pipelined_map(const void *in, const void *out, int64_t n, int op,
                                  int tile_elems, int stages, int tiles_per_block,
-                                 int resident_cap, int64_t lds_budget, tp_plan *plan)
+                                 int resident_cap, int schedule, int64_t lds_budget,
+                                 tp_plan *plan)
 {
     return tp::plan_map((uintptr_t)in, (uintptr_t)out, n, op, tile_elems, stages, tiles_per_block,
-                        resident_cap, lds_budget, plan);
+                        resident_cap, schedule, lds_budget, plan);
 }
 
 TP_API int tp_plan_chunk_copy(const void *src, const void *dst, int64_t n_chunks,
@@ -162,17 +163,17 @@ TP_API int tp_row_shift(const float *a, float *b, int64_t rows, void *stream, in
 TP_API int tp_pipelined_map(const float *in, float *out, int64_t n, int op, int tile_elems,
                             int stages, int tiles_per_block, void *stream, int *path_out)
 {
-    return tp_pipelined_map_ex(in, out, n, op, tile_elems, stages, tiles_per_block, 0, stream,
-                               path_out);
+    return tp_pipelined_map_ex(in, out, n, op, tile_elems, stages, tiles_per_block, 0,
+                               TP_SCHED_UNIFORM, stream, path_out);
 }
 
 TP_API int tp_pipelined_map_ex(const float *in, float *out, int64_t n, int op, int tile_elems,
-                               int stages, int tiles_per_block, int resident_cap, void *stream,
-                               int *path_out)
+                               int stages, int tiles_per_block, int resident_cap, int schedule,
+                               void *stream, int *path_out)
 {
     tp_plan plan;
     int st = tp::plan_map((uintptr_t)in, (uintptr_t)out, n, op, tile_elems, stages,
-                          tiles_per_block, resident_cap, kNoBudget, &plan);
+                          tiles_per_block, resident_cap, schedule, kNoBudget, &plan);
     if (st != TP_OK)
         return st;
     if (path_out)
@@ -185,7 +186,7 @@ TP_API int tp_pipelined_map_ex(const float *in, float *out, int64_t n, int op, i
     // again with the device's budget: the ring must fit, and the LDS reserved
     // to bound residency never exceeds it
     st = tp::plan_map((uintptr_t)in, (uintptr_t)out, n, op, tile_elems, stages, tiles_per_block,
-                      resident_cap, lds, &plan);
+                      resident_cap, schedule, lds, &plan);
     if (st != TP_OK)
         return st;
     tp::MapParams p;
@@ -197,10 +198,18 @@ TP_API int tp_pipelined_map_ex(const float *in, float *out, int64_t n, int op, i
     p.tiles_per_block = plan.tiles_per_block;
     tp::horner32_coefficients(p.coef);
     int e = 0;
-    switch (op) {
-    case TP_OP_SCALE2: e = tp::launch_map_scale2(plan, p, stream); break;
-    case TP_OP_HORNER32: e = tp::launch_map_horner32(plan, p, stream); break;
-    default: e = tp::launch_map_copy(plan, p, stream); break;
+    if (plan.schedule == TP_SCHED_ROLE_SPLIT) {
+        switch (op) {
+        case TP_OP_SCALE2: e = tp::launch_map_split_scale2(plan, p, stream); break;
+        case TP_OP_HORNER32: e = tp::launch_map_split_horner32(plan, p, stream); break;
+        default: e = tp::launch_map_split_copy(plan, p, stream); break;
+        }
+    } else {
+        switch (op) {
+        case TP_OP_SCALE2: e = tp::launch_map_scale2(plan, p, stream); break;
+        case TP_OP_HORNER32: e = tp::launch_map_horner32(plan, p, stream); break;
+        default: e = tp::launch_map_copy(plan, p, stream); break;
+        }
     }
     return finish_launch(e);
 }

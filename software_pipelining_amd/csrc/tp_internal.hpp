@@ -149,9 +149,10 @@ struct RowShiftParams {
 // Pure host code (no HIP): argument validation and launch geometry.
 int plan_row_shift(uintptr_t a, uintptr_t b, int64_t rows, int64_t lds_budget, tp_plan *plan);
 int plan_map(uintptr_t in, uintptr_t out, int64_t n, int op, int tile_elems, int stages,
-             int tiles_per_block, int resident_cap, int64_t lds_budget, tp_plan *plan);
+             int tiles_per_block, int resident_cap, int schedule, int64_t lds_budget,
+             tp_plan *plan);
 // The library's residency bound for a map launch (0: none); see tp_pipelined_map_ex.
-int map_policy_resident_cap(int op, int tile_elems, int stages, int tiles_per_block);
+int map_policy_resident_cap(int op, int tile_elems, int stages, int tiles_per_block, int waves);
 int plan_chunk_copy(uintptr_t src, uintptr_t dst, int64_t n_chunks, uintptr_t pred,
                     uintptr_t src_size, uintptr_t ignore_src, int stages, int tiles_per_block,
                     int64_t lds_budget, tp_plan *plan);
@@ -165,6 +166,9 @@ int launch_row_shift(const tp_plan &plan, const RowShiftParams &p, void *stream)
 int launch_map_scale2(const tp_plan &plan, const MapParams &p, void *stream);
 int launch_map_horner32(const tp_plan &plan, const MapParams &p, void *stream);
 int launch_map_copy(const tp_plan &plan, const MapParams &p, void *stream);
+int launch_map_split_scale2(const tp_plan &plan, const MapParams &p, void *stream);
+int launch_map_split_horner32(const tp_plan &plan, const MapParams &p, void *stream);
+int launch_map_split_copy(const tp_plan &plan, const MapParams &p, void *stream);
 int launch_chunk_copy(const tp_plan &plan, const ChunkParams &p, void *stream);
 
 }  // namespace tp

@@ -1,0 +1,11 @@
+// Role-split pipelined map kernels for op = scale2 (every stage count, tile size and path).
+#include "tp_map_split.hpp"
+
+namespace tp {
+
+int launch_map_split_scale2(const tp_plan &plan, const MapParams &p, void *stream)
+{
+    return dev::launch_map_split_op<TP_OP_SCALE2>(plan, p, stream);
+}
+
+}  // namespace tp

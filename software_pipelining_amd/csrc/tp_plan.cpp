@@ -60,7 +60,7 @@ int32_t reserve_for_cap(int32_t ring_bytes, int cap, int64_t lds_budget)
 
 }  // namespace
 
-int map_policy_resident_cap(int op, int tile_elems, int stages, int tiles_per_block)
+int map_policy_resident_cap(int op, int tile_elems, int stages, int tiles_per_block, int waves)
 {
     // A wave of the streaming ops is almost always waiting on memory, so the
     // resident workgroups decide how much traffic is in flight; past roughly
@@ -74,7 +74,6 @@ int map_policy_resident_cap(int op, int tile_elems, int stages, int tiles_per_bl
     const MapGeometry g = map_geometry(tile_elems);
     if (op == TP_OP_HORNER32 || tiles_per_block <= 1 || g.lane_chunks > 1)
         return 0;
-    const int waves = g.threads / 64;
     const double moving = mean_tiles_in_flight(tiles_per_block, stages) + 1.0;   // loads + stores
     const double target = kInflightTargetBytes * (1.0 + 1.0 / tiles_per_block);
     int cap = (int)(target / (moving * tile_elems * 4.0) + 0.5);
@@ -119,9 +118,10 @@ int plan_row_shift(uintptr_t a, uintptr_t b, int64_t rows, int64_t lds_budget, t
 }
 
 int plan_map(uintptr_t in, uintptr_t out, int64_t n, int op, int tile_elems, int stages,
-             int tiles_per_block, int resident_cap, int64_t lds_budget, tp_plan *plan)
+             int tiles_per_block, int resident_cap, int schedule, int64_t lds_budget,
+             tp_plan *plan)
 {
-    if (resident_cap < -1)
+    if (resident_cap < -1 || (schedule != TP_SCHED_UNIFORM && schedule != TP_SCHED_ROLE_SPLIT))
         return TP_ERR_INVALID_ARG;
     if (n < 0 || n > kMaxMapElems)
         return TP_ERR_INVALID_ARG;
@@ -141,8 +141,10 @@ int plan_map(uintptr_t in, uintptr_t out, int64_t n, int op, int tile_elems, int
     memset(&p, 0, sizeof p);
     p.stages = stages;
     p.tile_units = tile_elems;
-    p.threads = g.threads;
+    // the role split adds one wave that only loads
+    p.threads = g.threads + (schedule == TP_SCHED_ROLE_SPLIT ? 64 : 0);
     p.lane_chunks = g.lane_chunks;
+    p.schedule = schedule;
     p.tiles_per_block = tpb;
     p.ring_bytes = stages * tile_elems * 4 + kMapTailLdsBytes;
     if (n > 0) {
@@ -156,17 +158,24 @@ int plan_map(uintptr_t in, uintptr_t out, int64_t n, int op, int tile_elems, int
     }
     if (p.ring_bytes > lds_budget)
         return TP_ERR_LDS_BUDGET;
-    const int cap = resident_cap == 0 ? map_policy_resident_cap(op, tile_elems, stages, tpb)
+    const int waves = p.threads / 64;
+    const int cap = resident_cap == 0 ? map_policy_resident_cap(op, tile_elems, stages, tpb, waves)
                                       : resident_cap;
-    p.resident_cap = cap >= kMaxWavesPerCu / (g.threads / 64) ? 0 : (cap < 0 ? 0 : cap);
+    p.resident_cap = cap >= kMaxWavesPerCu / waves ? 0 : (cap < 0 ? 0 : cap);
     p.lds_bytes = p.resident_cap ? reserve_for_cap(p.ring_bytes, p.resident_cap, lds_budget)
                                  : p.ring_bytes;
     p.path = n > 0 ? path_bits(in, out) : TP_PATH_X4;
     const bool load_x4 = !(p.path & TP_PATH_SCALAR_LOAD);
     const bool store_x4 = !(p.path & TP_PATH_SCALAR_STORE);
-    p.wait_steady = stage_wait_count(stages, map_loads_per_tile(load_x4, g.lane_chunks),
-                                     map_stores_per_tile(store_x4, g.lane_chunks), stages,
-                                     map_wave_local(load_x4, store_x4));
+    if (schedule == TP_SCHED_ROLE_SPLIT) {
+        // the loading wave covers the whole tile and issues no stores
+        const int ld = map_loads_per_tile(load_x4, g.lane_chunks) * (g.threads / 64);
+        p.wait_steady = stages == 1 ? 0 : stage_wait_count(stages, ld, 0, 0);
+    } else {
+        p.wait_steady = stage_wait_count(stages, map_loads_per_tile(load_x4, g.lane_chunks),
+                                         map_stores_per_tile(store_x4, g.lane_chunks), stages,
+                                         map_wave_local(load_x4, store_x4));
+    }
     const int64_t n_main = n & ~int64_t(3);
     p.num_tiles = ceil_div(n_main, tile_elems);
     p.grid = n == 0 ? 0 : (p.num_tiles == 0 ? 1 : ceil_div(p.num_tiles, tpb));

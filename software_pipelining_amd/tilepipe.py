@@ -27,6 +27,22 @@ class Path(enum.IntEnum):
     SCALAR = 3
 
 
+class Schedule(enum.IntEnum):
+    UNIFORM = 0
+    ROLE_SPLIT = 1
+
+
+def _schedule(schedule) -> int:
+    """Schedule value for the C ABI; out-of-range integers pass through so the
+    library reports them."""
+    if isinstance(schedule, str):
+        try:
+            return int(Schedule[schedule.upper()])
+        except KeyError:
+            raise ValueError(f"unknown schedule {schedule!r}; expected 'uniform' or 'role_split'")
+    return int(schedule)
+
+
 class TilepipeError(RuntimeError):
     def __init__(self, status: int, where: str = "", hip_error: int = 0):
         self.status = status
@@ -44,7 +60,8 @@ class _CPlan(ctypes.Structure):
                 ("lane_chunks", ctypes.c_int32), ("tiles_per_block", ctypes.c_int32),
                 ("lds_bytes", ctypes.c_int32), ("wait_steady", ctypes.c_int32),
                 ("num_tiles", ctypes.c_int64), ("grid", ctypes.c_int64),
-                ("ring_bytes", ctypes.c_int32), ("resident_cap", ctypes.c_int32)]
+                ("ring_bytes", ctypes.c_int32), ("resident_cap", ctypes.c_int32),
+                ("schedule", ctypes.c_int32)]
 
 
 @dataclass(frozen=True)
@@ -61,6 +78,7 @@ class Plan:
     grid: int
     ring_bytes: int
     resident_cap: int
+    schedule: "Schedule"
 
 
 _lib = None
@@ -90,10 +108,10 @@ def _load():
         "tp_device_lds_budget": ([i32, ctypes.POINTER(ctypes.c_int64)], i32),
         "tp_row_shift": ([vp, vp, i64, vp, ip], i32),
         "tp_pipelined_map": ([vp, vp, i64, i32, i32, i32, i32, vp, ip], i32),
-        "tp_pipelined_map_ex": ([vp, vp, i64, i32, i32, i32, i32, i32, vp, ip], i32),
+        "tp_pipelined_map_ex": ([vp, vp, i64, i32, i32, i32, i32, i32, i32, vp, ip], i32),
         "tp_chunk_copy": ([vp, vp, i64, vp, vp, vp, i32, i32, vp, ip], i32),
         "tp_plan_row_shift": ([vp, vp, i64, i64, pp], i32),
-        "tp_plan_pipelined_map": ([vp, vp, i64, i32, i32, i32, i32, i32, i64, pp], i32),
+        "tp_plan_pipelined_map": ([vp, vp, i64, i32, i32, i32, i32, i32, i32, i64, pp], i32),
         "tp_plan_chunk_copy": ([vp, vp, i64, vp, vp, vp, i32, i32, i64, pp], i32),
     }
     for name, (args, res) in sig.items():
@@ -169,12 +187,15 @@ def row_shift(a, b=None, stream=None) -> Path:
 
 
 def pipelined_map(x, y=None, op: str = "scale2", tile_elems: int = 1024, stages: int = 2,
-                  tiles_per_block: int = 0, stream=None, resident_cap: int = 0) -> Path:
+                  tiles_per_block: int = 0, stream=None, resident_cap: int = 0,
+                  schedule: "Schedule | str" = "uniform") -> Path:
     """y[i] = op(x[i]) for float32 GPU tensors (any shape, contiguous).
 
     Each workgroup streams tiles_per_block consecutive tiles (0: the
     library default of 2). resident_cap bounds the workgroups per CU
-    (0: the library's policy, -1: no bound, k: at most k)."""
+    (0: the library's policy, -1: no bound, k: about k). schedule "uniform"
+    (every wave loads its own part) or "role_split" (one wave loads, the
+    others compute)."""
     import torch
     if op not in OPS:
         raise ValueError(f"unknown op {op!r}; expected one of {sorted(OPS)}")
@@ -190,7 +211,8 @@ def pipelined_map(x, y=None, op: str = "scale2", tile_elems: int = 1024, stages:
         st = _load().tp_pipelined_map_ex(ctypes.c_void_p(x.data_ptr()),
                                          ctypes.c_void_p(y.data_ptr()), x.numel(), OPS[op],
                                          tile_elems, stages, tiles_per_block, resident_cap,
-                                         _stream_handle(x, stream), ctypes.byref(path))
+                                         _schedule(schedule), _stream_handle(x, stream),
+                                         ctypes.byref(path))
     _check(st, "tp_pipelined_map_ex")
     return Path(path.value)
 
@@ -232,7 +254,7 @@ def _plan(status: int, cp: _CPlan, where: str) -> Plan:
     _check(status, where)
     return Plan(Path(cp.path), cp.stages, cp.tile_units, cp.threads, cp.lane_chunks,
                 cp.tiles_per_block, cp.lds_bytes, cp.wait_steady, cp.num_tiles, cp.grid,
-                cp.ring_bytes, cp.resident_cap)
+                cp.ring_bytes, cp.resident_cap, Schedule(cp.schedule))
 
 
 def plan_row_shift(a_ptr: int, b_ptr: int, rows: int, lds_budget: int = _NO_BUDGET) -> Plan:
@@ -244,12 +266,12 @@ def plan_row_shift(a_ptr: int, b_ptr: int, rows: int, lds_budget: int = _NO_BUDG
 
 def plan_map(in_ptr: int, out_ptr: int, n: int, op: str = "scale2", tile_elems: int = 1024,
              stages: int = 2, tiles_per_block: int = 0, lds_budget: int = _NO_BUDGET,
-             resident_cap: int = 0) -> Plan:
+             resident_cap: int = 0, schedule: "Schedule | str" = "uniform") -> Plan:
     cp = _CPlan()
     st = _load().tp_plan_pipelined_map(ctypes.c_void_p(in_ptr), ctypes.c_void_p(out_ptr), n,
                                        OPS.get(op, op if isinstance(op, int) else -1),
                                        tile_elems, stages, tiles_per_block, resident_cap,
-                                       lds_budget, ctypes.byref(cp))
+                                       _schedule(schedule), lds_budget, ctypes.byref(cp))
     return _plan(st, cp, "tp_plan_pipelined_map")
 
 

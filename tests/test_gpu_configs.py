@@ -84,7 +84,9 @@ def test_config5_horner32(cuda_device):
     x = x_host.to(cuda_device)
     y = torch.empty_like(x)
     for stages in (1, 2, 4):
-        for tpb in (0, 16, 64):
+        for tpb, cap, schedule in ((0, 0, "uniform"), (16, 0, "uniform"), (64, 0, "uniform"),
+                                   (8, 2, "uniform"), (0, 0, "role_split"), (8, 2, "role_split")):
             y.fill_(float("nan"))
-            tp.pipelined_map(x, y, "horner32", 1024, stages, tpb)
-            assert_equal_on_device(y, exp, f"config 5 S={stages} T={tpb}")
+            tp.pipelined_map(x, y, "horner32", 1024, stages, tpb, resident_cap=cap,
+                             schedule=schedule)
+            assert_equal_on_device(y, exp, f"config 5 {schedule} S={stages} T={tpb} cap={cap}")

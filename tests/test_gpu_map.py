@@ -27,29 +27,32 @@ def _expected_path(in_off, out_off):
     return (tp.Path.SCALAR_LOAD if in_off % 4 else 0) | (tp.Path.SCALAR_STORE if out_off % 4 else 0)
 
 
-def _run_case(dev, op, x_host, expected, in_off, out_off, tile, stages, tpb, budget):
+def _run_case(dev, op, x_host, expected, in_off, out_off, tile, stages, tpb, budget,
+              schedule="uniform"):
     n = x_host.numel()
     x = to_device(x_host, dev, offset_words=in_off)
     y = out_buffer(n, torch.float32, dev, offset_words=out_off)
-    plan = tp.plan_map(x.tensor.data_ptr(), y.tensor.data_ptr(), n, op, tile, stages, tpb)
+    plan = tp.plan_map(x.tensor.data_ptr(), y.tensor.data_ptr(), n, op, tile, stages, tpb,
+                       schedule=schedule)
     if plan.ring_bytes > budget and n > 0:     # an empty call launches nothing, so it succeeds
         with pytest.raises(tp.TilepipeError) as e:
-            tp.pipelined_map(x.tensor, y.tensor, op, tile, stages, tpb)
+            tp.pipelined_map(x.tensor, y.tensor, op, tile, stages, tpb, schedule=schedule)
         assert e.value.status == 3
         return False
-    path = tp.pipelined_map(x.tensor, y.tensor, op, tile, stages, tpb)
+    path = tp.pipelined_map(x.tensor, y.tensor, op, tile, stages, tpb, schedule=schedule)
     if n:
         assert path == _expected_path(in_off, out_off)
-    what = f"{op} n={n} tile={tile} S={stages} T={tpb} path={int(path)}"
+    what = f"{op} {schedule} n={n} tile={tile} S={stages} T={tpb} path={int(path)}"
     assert_bits_equal(y.tensor, expected, what, nan_free=False)
     assert y.guards_intact(), what + ": write outside the output"
     assert x.guards_intact(), what + ": input region changed"
     return True
 
 
+@pytest.mark.parametrize("schedule", ["uniform", "role_split"])
 @pytest.mark.parametrize("op", OPS)
 @pytest.mark.parametrize("in_off,out_off", PATH_OFFSETS)
-def test_map_parity_sizes_stages_tiles(cuda_device, op, in_off, out_off):
+def test_map_parity_sizes_stages_tiles(cuda_device, op, in_off, out_off, schedule):
     budget = tp.lds_budget(0)
     ran = 0
     for n in SIZES:
@@ -58,12 +61,13 @@ def test_map_parity_sizes_stages_tiles(cuda_device, op, in_off, out_off):
         for tile in TILES:
             for stages in STAGES:
                 ran += _run_case(cuda_device, op, x_host, expected, in_off, out_off, tile,
-                                 stages, 0, budget)
+                                 stages, 0, budget, schedule)
     assert ran > 0
 
 
+@pytest.mark.parametrize("schedule", ["uniform", "role_split"])
 @pytest.mark.parametrize("op", OPS)
-def test_map_tiles_per_block(cuda_device, op):
+def test_map_tiles_per_block(cuda_device, op, schedule):
     budget = tp.lds_budget(0)
     n = 3 * 4096 * 5 + 13
     x_host = workloads.uniform_pm1(n, seed=77)
@@ -71,7 +75,8 @@ def test_map_tiles_per_block(cuda_device, op):
     for tpb in (1, 2, 3, 7, 64, 1000):
         for stages in (1, 2, 4, 7):
             for tile in (256, 4096):
-                _run_case(cuda_device, op, x_host, expected, 0, 0, tile, stages, tpb, budget)
+                _run_case(cuda_device, op, x_host, expected, 0, 0, tile, stages, tpb, budget,
+                          schedule)
 
 
 @pytest.mark.parametrize("op", OPS)
@@ -95,11 +100,12 @@ def test_map_in_place(cuda_device, op):
     n = 5 * 1024 + 3
     x_host = workloads.uniform_pm1(n, seed=31)
     expected = oracle.pipelined_map(x_host.numpy(), op)
-    for stages in (1, 2, 4):
-        x = to_device(x_host, cuda_device)
-        tp.pipelined_map(x.tensor, x.tensor, op, 1024, stages, 2)
-        assert_bits_equal(x.tensor, expected, f"in place S={stages}")
-        assert x.guards_intact()
+    for schedule in ("uniform", "role_split"):
+        for stages in (1, 2, 4):
+            x = to_device(x_host, cuda_device)
+            tp.pipelined_map(x.tensor, x.tensor, op, 1024, stages, 2, schedule=schedule)
+            assert_bits_equal(x.tensor, expected, f"in place {schedule} S={stages}")
+            assert x.guards_intact()
 
 
 def test_map_results_identical_across_parameters(cuda_device):
@@ -110,14 +116,15 @@ def test_map_results_identical_across_parameters(cuda_device):
     budget = tp.lds_budget(0)
     for tile in (256, 1024, 8192):
         for stages in (1, 2, 3, 6):
-            for tpb in (1, 64):
+            for tpb, schedule in ((1, "uniform"), (64, "uniform"), (3, "role_split")):
                 for in_off, out_off in PATH_OFFSETS:
                     x = to_device(x_host, cuda_device, offset_words=in_off)
                     y = out_buffer(n, torch.float32, cuda_device, offset_words=out_off)
                     if tp.plan_map(x.tensor.data_ptr(), y.tensor.data_ptr(), n, "horner32", tile,
                                    stages, tpb).ring_bytes > budget:
                         continue
-                    tp.pipelined_map(x.tensor, y.tensor, "horner32", tile, stages, tpb)
+                    tp.pipelined_map(x.tensor, y.tensor, "horner32", tile, stages, tpb,
+                                     schedule=schedule)
                     got = y.tensor.cpu()
                     if ref is None:
                         ref = got
@@ -131,13 +138,15 @@ def test_map_residency_bound_keeps_results(cuda_device, op):
     n = 7 * 4096 * 3 + 5
     x_host = workloads.uniform_pm1(n, seed=55)
     expected = oracle.pipelined_map(x_host.numpy(), op)
-    for tile, stages, tpb in ((256, 2, 2), (1024, 4, 3), (4096, 2, 1)):
+    for tile, stages, tpb, schedule in ((256, 2, 2, "uniform"), (1024, 4, 3, "uniform"),
+                                        (4096, 2, 1, "uniform"), (1024, 2, 4, "role_split")):
         for cap in (-1, 0, 1, 2, 3, 17, 40):
             for in_off, out_off in ((0, 0), (1, 0)):
                 x = to_device(x_host, cuda_device, offset_words=in_off)
                 y = out_buffer(n, torch.float32, cuda_device, offset_words=out_off)
-                tp.pipelined_map(x.tensor, y.tensor, op, tile, stages, tpb, resident_cap=cap)
-                what = f"{op} tile={tile} S={stages} T={tpb} cap={cap} in_off={in_off}"
+                tp.pipelined_map(x.tensor, y.tensor, op, tile, stages, tpb, resident_cap=cap,
+                                 schedule=schedule)
+                what = f"{op} {schedule} tile={tile} S={stages} T={tpb} cap={cap} in_off={in_off}"
                 assert_bits_equal(y.tensor, expected, what, nan_free=False)
                 assert y.guards_intact() and x.guards_intact(), what
 
@@ -155,4 +164,7 @@ def test_map_errors(cuda_device):
     assert e.value.status == 3
     with pytest.raises(tp.TilepipeError) as e:
         tp.pipelined_map(x, torch.empty_like(x), "scale2", 1024, 2, resident_cap=-2)
+    assert e.value.status == 1
+    with pytest.raises(tp.TilepipeError) as e:
+        tp.pipelined_map(x, torch.empty_like(x), "scale2", 1024, 2, schedule=5)
     assert e.value.status == 1

@@ -213,6 +213,29 @@ def test_map_explicit_residency():
     assert _status(tp.plan_map, A, B, 10, "scale2", 1024, 2, 2, tilepipe._NO_BUDGET, -2) == 1
 
 
+def test_map_role_split_plan():
+    # one more wave that only loads; its wait counts only its own loads of the
+    # S-2 tiles issued after the waited one (it issues no stores)
+    for tile, threads, per_tile in [(256, 128, 1), (512, 192, 2), (1024, 320, 4), (2048, 320, 8),
+                                    (4096, 320, 16), (8192, 320, 32)]:
+        for S in (1, 2, 3, 4):
+            p = tp.plan_map(A, B, 1 << 20, "horner32", tile, S, 2, schedule="role_split")
+            assert p.schedule == tp.Schedule.ROLE_SPLIT and p.threads == threads
+            assert p.wait_steady == min(63, (S - 2) * per_tile) if S > 1 else p.wait_steady == 0
+            q = tp.plan_map(A + 4, B, 1 << 20, "horner32", tile, S, 2, schedule="role_split")
+            assert q.wait_steady == (min(63, (S - 2) * 4 * per_tile) if S > 1 else 0)
+            u = tp.plan_map(A, B, 1 << 20, "horner32", tile, S, 2)
+            assert (u.schedule, u.threads) == (tp.Schedule.UNIFORM, threads - 64)
+            assert (p.ring_bytes, p.grid, p.num_tiles) == (u.ring_bytes, u.grid, u.num_tiles)
+    # residency counts the extra wave: tile 1024 has 5 waves per workgroup, 6 fit a CU
+    p = tp.plan_map(A, B, 1 << 26, "scale2", 1024, 2, 2, schedule="role_split")
+    assert p.resident_cap == 4
+    p = tp.plan_map(A, B, 1 << 26, "scale2", 1024, 2, 2, resident_cap=6, schedule="role_split")
+    assert p.resident_cap == 0        # 6 x 5 waves already fill 32 wave slots
+    assert _status(tp.plan_map, A, B, 10, "scale2", 1024, 2, 2, tilepipe._NO_BUDGET, 0, 2) == 1
+    assert _status(tp.plan_map, A, B, 10, "scale2", 1024, 2, 2, tilepipe._NO_BUDGET, 0, -1) == 1
+
+
 # ------------------------------------------------------------ row shift
 def test_row_shift_plan():
     p = tp.plan_row_shift(A, B, 64)
