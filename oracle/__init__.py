@@ -57,6 +57,8 @@ def _load():
     lib.oracle_horner32_subnormal_steps.restype = i64
     lib.oracle_chunk_copy.argtypes = [p, p, p, p, p, i64, i64]
     lib.oracle_chunk_copy.restype = None
+    lib.oracle_map_2d.argtypes = [p, i64, p, i64, i64, ctypes.c_int, i64, i64]
+    lib.oracle_map_2d.restype = None
     _lib = lib
     return lib
 
@@ -123,6 +125,41 @@ def pipelined_map(x: np.ndarray, op: str = "scale2", threads: int | None = None,
     fn = getattr(_load(), _MAP_FN[op])
     _run_ranged(fn, (_ptr(x), _ptr(out)), x.size, threads or default_threads())
     return out
+
+
+_OP_CODE = {"scale2": 0, "horner32": 1, "copy": 2}
+
+
+def map_2d(src: np.ndarray, dst: np.ndarray, op: str = "scale2",
+           threads: int | None = None) -> np.ndarray:
+    """dst[r, c] = op(src[r, c]) for 2-D float32 views with unit column stride
+    (rows may lie any number of elements apart); writes into dst in place and
+    returns it. Elements of dst's underlying buffer outside the view are not
+    touched."""
+    if op not in _OP_CODE:
+        raise ValueError(f"unknown op {op!r}")
+    for a in (src, dst):
+        if a.ndim != 2 or a.dtype != np.float32 or (a.shape[1] > 1 and a.strides[1] != 4) \
+                or a.strides[0] < 0 or a.strides[0] % 4:
+            raise ValueError("map_2d expects 2-D float32 views with unit column stride")
+    if src.shape != dst.shape:
+        raise ValueError("src and dst must have the same shape")
+    rows, cols = src.shape
+    if rows == 0 or cols == 0:
+        return dst
+    lib = _load()
+    args = (src.ctypes.data, src.strides[0] // 4, dst.ctypes.data, dst.strides[0] // 4, cols,
+            _OP_CODE[op])
+    threads = threads or default_threads()
+    parts = max(1, min(threads, rows, (rows * cols + (1 << 16) - 1) >> 16))
+    step = -(-rows // parts)
+    rs = [(lo, min(rows, lo + step)) for lo in range(0, rows, step)]
+    if len(rs) == 1:
+        lib.oracle_map_2d(*args, 0, rows)
+    else:
+        with ThreadPoolExecutor(max_workers=len(rs)) as ex:
+            list(ex.map(lambda r: lib.oracle_map_2d(*args, r[0], r[1]), rs))
+    return dst
 
 
 def horner32_coeffs() -> np.ndarray:

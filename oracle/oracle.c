@@ -92,6 +92,30 @@ void oracle_map_horner32(const float *in, float *out, int64_t lo, int64_t hi)
 }
 
 /*
+ * Strided 2-D map: the maps above applied to a window of a row-major matrix
+ * whose rows lie a stride apart, the tile described by a base, a shape and
+ * strides ("Asynchronous Data Movement", section "The Tensor Memory
+ * Accelerator"):
+ *   dst[r * dst_stride + c] = op(src[r * src_stride + c]),  lo <= r < hi, 0 <= c < cols
+ * op: 0 scale2, 1 horner32, 2 copy. Elements of dst outside the window are
+ * not written. Rows are independent, so [lo, hi) splits the rows over threads.
+ */
+void oracle_map_2d(const float *src, int64_t src_stride, float *dst, int64_t dst_stride,
+                   int64_t cols, int op, int64_t lo, int64_t hi)
+{
+    for (int64_t r = lo; r < hi; ++r) {
+        const float *s = src + r * src_stride;
+        float *d = dst + r * dst_stride;
+        if (op == 0)
+            oracle_map_scale2(s, d, 0, cols);
+        else if (op == 1)
+            oracle_map_horner32(s, d, 0, cols);
+        else
+            oracle_map_copy(s, d, 0, cols);
+    }
+}
+
+/*
  * Diagnostic for the rounding reading: how many Horner steps over [lo, hi)
  * produce a subnormal result or a subnormal (nonzero) exact product y*x.
  * If this is zero on a workload, a flush-to-zero mode on either side could not

@@ -205,6 +205,58 @@ def test_map_range_split_does_not_change_results():
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
+# ---------------------------------------------------------------- 2-D map
+def _window(rng, rows, cols, pad_cols, row0=2, col0=3):
+    """A (rows, cols) view at (row0, col0) of a larger row-major buffer."""
+    buf = rng.standard_normal((rows + row0 + 1, cols + col0 + pad_cols)).astype(np.float32)
+    return buf, buf[row0:row0 + rows, col0:col0 + cols]
+
+
+@pytest.mark.parametrize("rows,cols,spad,dpad", [(1, 1, 0, 0), (7, 13, 5, 0), (33, 64, 1, 9),
+                                                  (5, 300, 17, 3), (64, 4, 60, 0)])
+def test_map_2d_copy_and_scale2_equal_numpy_slices(rows, cols, spad, dpad):
+    # a library routine (numpy slicing, exact multiply by two) on the same window
+    rng = np.random.default_rng(rows * 1000 + cols)
+    sbuf, src = _window(rng, rows, cols, spad)
+    for op, ref in (("copy", lambda a: a.copy()), ("scale2", lambda a: a * np.float32(2))):
+        dbuf, dst = _window(rng, rows, cols, dpad, row0=1, col0=0)
+        before = dbuf.copy()
+        oracle.map_2d(src, dst, op)
+        expect = before.copy()
+        expect[1:1 + rows, 0:cols] = ref(src)
+        assert np.array_equal(dbuf.view(np.uint32), expect.view(np.uint32)), op
+
+
+def test_map_2d_reduces_to_the_1d_map():
+    # a contiguous window (stride == cols) is the 1-D map over rows*cols floats,
+    # and any strided window is the 1-D map of its gathered elements
+    x = workloads.uniform_pm1(37 * 29, seed=9).numpy()
+    for op in ("scale2", "horner32", "copy"):
+        dst = np.zeros((37, 29), np.float32)
+        oracle.map_2d(x.reshape(37, 29), dst, op)
+        assert np.array_equal(dst.reshape(-1).view(np.uint32),
+                              oracle.pipelined_map(x, op).view(np.uint32))
+    rng = np.random.default_rng(5)
+    sbuf, src = _window(rng, 40, 50, 11)
+    dbuf, dst = _window(rng, 40, 50, 3)
+    oracle.map_2d(src, dst, "horner32", threads=3)
+    gathered = oracle.pipelined_map(np.ascontiguousarray(src).reshape(-1), "horner32")
+    assert np.array_equal(np.ascontiguousarray(dst).reshape(-1).view(np.uint32),
+                          gathered.view(np.uint32))
+
+
+def test_map_2d_empty_and_untouched():
+    rng = np.random.default_rng(1)
+    sbuf, src = _window(rng, 9, 9, 2)
+    dbuf, _ = _window(rng, 9, 9, 2)
+    before = dbuf.copy()
+    oracle.map_2d(src[:0], dbuf[2:2, 3:12], "scale2")
+    oracle.map_2d(src[:, :0], dbuf[2:11, 3:3], "scale2")
+    assert np.array_equal(dbuf.view(np.uint32), before.view(np.uint32))
+    with pytest.raises(ValueError):
+        oracle.map_2d(src, dbuf[2:11, 3:11], "scale2")      # shapes differ
+
+
 # -------------------------------------------------------------- chunk copy
 def _golden_chunk_cases():
     cases = []
