@@ -370,6 +370,41 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+MAP2D_ROWS, MAP2D_COLS, MAP2D_SRC_STRIDE = 16384, 16384, 16448
+MAP2D_BOXES = [(1, 256), (4, 256), (1, 1024), (2, 512), (8, 128), (16, 64), (4, 1024)]
+
+
+def map_2d_row(tp, workloads, torch, np, dev, scratch):
+    """scale2 over a 16384 x 16384 fp32 window (1 GiB) of a source whose rows
+    are 16448 floats apart, into a dense destination, for several box shapes
+    at 2 stages and runs of 2; sampled rows checked against the oracle."""
+    import oracle
+    R, C, SS = MAP2D_ROWS, MAP2D_COLS, MAP2D_SRC_STRIDE
+    src_h = workloads.uniform_pm1(R * SS, seed=6)
+    src = src_h.to(dev).view(R, SS)[:, :C]
+    dst = torch.empty(R, C, dtype=torch.float32, device=dev)
+    out = {"workload": f"scale2 over a {R} x {C} fp32 window (row stride {SS}) into a dense "
+                       f"{R} x {C} destination; 2 stages, runs of 2 boxes", "boxes": {}}
+    gpu_warmup(lambda: tp.map_2d(src, dst, "scale2", 4, 256, 2, 0))
+    for br, bc in MAP2D_BOXES:
+        f = lambda: tp.map_2d(src, dst, "scale2", br, bc, 2, 0)
+        f()
+        per, _ = time_launches(f, 2, 10)
+        gbs = 8 * R * C / (median(per) * 1e-3) / 1e9
+        out["boxes"][f"{br}x{bc}"] = {"GBs": round(gbs, 1), "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1)}
+    # parity of the last launch on sampled rows
+    rng = np.random.default_rng(0)
+    sh = src_h.numpy().reshape(R, SS)
+    ok = True
+    for r in rng.integers(0, R, size=12):
+        exp = oracle.pipelined_map(sh[r, :C], "scale2", threads=1)
+        ok &= bool(np.array_equal(dst[r].cpu().numpy().view(np.uint32), exp.view(np.uint32)))
+    out["parity_sampled_rows"] = ok
+    del src, dst
+    log(f"map_2d: {out['boxes']}")
+    return out
+
+
 def extra_rows(args, tp, workloads, torch, np, dev, x_host, xbuf, y):
     rows = {}
     n = x_host.numel()
@@ -469,6 +504,8 @@ def extra_rows(args, tp, workloads, torch, np, dev, x_host, xbuf, y):
     rows["horner32"] = hr
     log(f"horner32: {hr}")
     del xh, yh
+
+    rows["map_2d"] = map_2d_row(tp, workloads, torch, np, dev, y)
 
     # predicated chunk copy: 2^26 chunks. Not timed on the GPU in this test
     # window (it faulted twice before its wait-state hazard was found and fixed).

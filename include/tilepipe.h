@@ -186,6 +186,36 @@ TP_API int tp_pipelined_map_ex(const float *in, float *out, int64_t n, int op,
                                int resident_cap, int schedule, void *stream, int *path_out);
 
 /*
+ * Strided 2-D map ("Asynchronous Data Movement", section "The Tensor Memory
+ * Accelerator": a tile transfer described by a base, a shape and strides
+ * rather than by per-thread addresses):
+ *     dst[r * dst_stride + c] = op(src[r * src_stride + c]),  0 <= r < rows, 0 <= c < cols.
+ * src, dst: device float32 buffers; strides in elements, cols <= stride <= 2^36.
+ * The window is cut into boxes of box_rows x box_cols floats (powers of two,
+ * box_cols >= 4, box_rows * box_cols one of 256 .. 8192; 0 x 0 picks boxes of
+ * 1024 floats as wide as the window allows: box_cols the smallest power of
+ * two >= min(cols, 1024), at least 4, box_rows = 1024 / box_cols); a workgroup streams
+ * boxes_per_block boxes side by side in one band of box_rows rows (0: the
+ * default of 2) through an LDS ring of `stages` slots, each box read by
+ * LDS-DMA loads from row * stride + column. Elements of an edge box outside
+ * the matrix are neither read nor written, and dst outside the window is not
+ * touched. Each side uses 16-byte accesses when its pointer is 16-byte
+ * aligned and its stride and cols are multiples of 4, else 4-byte accesses
+ * (reported in path_out; bit 0 loads, bit 1 stores). The library's bound on
+ * resident workgroups per CU (tp_pipelined_map_ex) applies. Errors:
+ * TP_ERR_INVALID_ARG (bad shape, box, stages, a band of box_rows rows up to
+ * the run's last column spanning more than 1 GiB on either side, or more than
+ * 2^31 - 1 workgroups), TP_ERR_MISALIGNED (a pointer not 4-byte aligned),
+ * TP_ERR_OVERLAP (the byte ranges of the windows overlap, unless dst == src
+ * with equal strides, which is allowed), TP_ERR_LDS_BUDGET (stages x box bytes
+ * exceeds the device's LDS per workgroup). rows or cols 0: TP_OK, nothing
+ * launched (pointers may then be NULL).
+ */
+TP_API int tp_map_2d(const float *src, int64_t src_stride, float *dst, int64_t dst_stride,
+                     int64_t rows, int64_t cols, int op, int box_rows, int box_cols,
+                     int stages, int boxes_per_block, void *stream, int *path_out);
+
+/*
  * Predicated 16-byte chunk copy ("Asynchronous Copies", section "A
  * Global-to-Shared Copy", the paragraph on pred, src_size and ignore_src).
  * For each chunk i < n_chunks:
@@ -219,6 +249,10 @@ TP_API int tp_plan_pipelined_map(const void *in, const void *out, int64_t n, int
                                  int tile_elems, int stages, int tiles_per_block,
                                  int resident_cap, int schedule, int64_t lds_budget,
                                  tp_plan *plan);
+TP_API int tp_plan_map_2d(const void *src, int64_t src_stride, const void *dst,
+                          int64_t dst_stride, int64_t rows, int64_t cols, int op, int box_rows,
+                          int box_cols, int stages, int boxes_per_block, int64_t lds_budget,
+                          tp_plan *plan);
 TP_API int tp_plan_chunk_copy(const void *src, const void *dst, int64_t n_chunks,
                               const void *pred, const void *src_size,
                               const void *ignore_src, int stages, int tiles_per_block,

@@ -38,7 +38,8 @@ CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wex
 
 HIP_SOURCES = ["tp_row_shift.hip", "tp_chunk_copy.hip", "tp_map_scale2.hip",
                "tp_map_horner32.hip", "tp_map_copy.hip", "tp_map_split_scale2.hip",
-               "tp_map_split_horner32.hip", "tp_map_split_copy.hip", "tp_api.cpp"]
+               "tp_map_split_horner32.hip", "tp_map_split_copy.hip", "tp_map2d_scale2.hip",
+               "tp_map2d_horner32.hip", "tp_map2d_copy.hip", "tp_api.cpp"]
 CXX_SOURCES = ["tp_plan.cpp"]
 
 

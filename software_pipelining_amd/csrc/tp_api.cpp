@@ -132,6 +132,15 @@ TP_API int tp_plan_pipelined_map(const void *in, const void *out, int64_t n, int
                         resident_cap, schedule, lds_budget, plan);
 }
 
+TP_API int tp_plan_map_2d(const void *src, int64_t src_stride, const void *dst,
+                          int64_t dst_stride, int64_t rows, int64_t cols, int op, int box_rows,
+                          int box_cols, int stages, int boxes_per_block, int64_t lds_budget,
+                          tp_plan *plan)
+{
+    return tp::plan_map_2d((uintptr_t)src, src_stride, (uintptr_t)dst, dst_stride, rows, cols, op,
+                           box_rows, box_cols, stages, boxes_per_block, lds_budget, plan);
+}
+
 TP_API int tp_plan_chunk_copy(const void *src, const void *dst, int64_t n_chunks,
                               const void *pred, const void *src_size, const void *ignore_src,
                               int stages, int tiles_per_block, int64_t lds_budget, tp_plan *plan)
@@ -210,6 +219,52 @@ TP_API int tp_pipelined_map_ex(const float *in, float *out, int64_t n, int op, i
         case TP_OP_HORNER32: e = tp::launch_map_horner32(plan, p, stream); break;
         default: e = tp::launch_map_copy(plan, p, stream); break;
         }
+    }
+    return finish_launch(e);
+}
+
+TP_API int tp_map_2d(const float *src, int64_t src_stride, float *dst, int64_t dst_stride,
+                     int64_t rows, int64_t cols, int op, int box_rows, int box_cols, int stages,
+                     int boxes_per_block, void *stream, int *path_out)
+{
+    tp_plan plan;
+    int st = tp::plan_map_2d((uintptr_t)src, src_stride, (uintptr_t)dst, dst_stride, rows, cols,
+                             op, box_rows, box_cols, stages, boxes_per_block, kNoBudget, &plan);
+    if (st != TP_OK)
+        return st;
+    if (path_out)
+        *path_out = plan.path;
+    if (plan.grid == 0)
+        return TP_OK;
+    int64_t lds = 0;
+    if ((st = current_device(&lds)) != TP_OK)
+        return st;
+    st = tp::plan_map_2d((uintptr_t)src, src_stride, (uintptr_t)dst, dst_stride, rows, cols, op,
+                         box_rows, box_cols, stages, boxes_per_block, lds, &plan);
+    if (st != TP_OK)
+        return st;
+    tp::Map2dParams p;
+    memset(&p, 0, sizeof p);
+    p.src = src;
+    p.dst = dst;
+    p.src_stride = src_stride;
+    p.dst_stride = dst_stride;
+    p.rows = rows;
+    p.cols = cols;
+    tp::map2d_resolve_box(cols, &box_rows, &box_cols);
+    int lg = 0;
+    while ((1 << lg) < box_cols)
+        ++lg;
+    p.box_cols_log2 = lg;
+    p.tiles_per_block = plan.tiles_per_block;
+    p.runs_per_band = (int32_t)((((cols + box_cols - 1) / box_cols) + plan.tiles_per_block - 1) /
+                                plan.tiles_per_block);
+    tp::horner32_coefficients(p.coef);
+    int e = 0;
+    switch (op) {
+    case TP_OP_SCALE2: e = tp::launch_map2d_scale2(plan, p, stream); break;
+    case TP_OP_HORNER32: e = tp::launch_map2d_horner32(plan, p, stream); break;
+    default: e = tp::launch_map2d_copy(plan, p, stream); break;
     }
     return finish_launch(e);
 }

@@ -25,6 +25,7 @@ constexpr int kMapTailLdsBytes = 256;      // LDS area for the final partial 16-
 constexpr int kVmcntMax = 63;              // vmcnt is a 6-bit counter on gfx9-family parts
 constexpr int64_t kMaxMapElems = int64_t(1) << 40;
 constexpr int64_t kMaxChunks = int64_t(1) << 36;
+constexpr int64_t kMaxStride = int64_t(1) << 36;     // elements between rows of a 2-D window
 constexpr int64_t kMaxRunBytes = int64_t(1) << 30;   // bytes one workgroup streams
 constexpr int kLdsPerCu = 160 * 1024;      // gfx950: LDS of one CU, all of it usable by one workgroup
 constexpr int kMaxWavesPerCu = 32;         // gfx950: 8 wave slots on each of 4 SIMDs
@@ -96,6 +97,20 @@ struct MapParams {
     float coef[32];          // Horner coefficients (used by TP_OP_HORNER32 only)
 };
 
+struct Map2dParams {
+    const float *src;
+    float *dst;
+    int64_t src_stride;      // elements between rows
+    int64_t dst_stride;
+    int64_t rows;
+    int64_t cols;
+    int32_t box_cols_log2;   // box_cols = 1 << box_cols_log2; box_rows follows from the tile size
+    int32_t tiles_per_block; // boxes per workgroup, side by side in one band of box_rows rows
+    int32_t runs_per_band;   // workgroups per band
+    int32_t pad;
+    float coef[32];          // Horner coefficients (used by TP_OP_HORNER32 only)
+};
+
 // ---------------------------------------------------------- chunk copy
 TP_HD constexpr int chunk_loads_per_tile(bool load_x4)
 {
@@ -153,6 +168,13 @@ int plan_map(uintptr_t in, uintptr_t out, int64_t n, int op, int tile_elems, int
              tp_plan *plan);
 // The library's residency bound for a map launch (0: none); see tp_pipelined_map_ex.
 int map_policy_resident_cap(int op, int tile_elems, int stages, int tiles_per_block, int waves);
+// Box of a 2-D map when the caller passes 0 x 0: 1024 floats, as wide as the
+// window allows (box_cols the smallest power of two >= min(cols, 1024), at
+// least 4). Leaves the arguments alone otherwise.
+void map2d_resolve_box(int64_t cols, int *box_rows, int *box_cols);
+int plan_map_2d(uintptr_t src, int64_t src_stride, uintptr_t dst, int64_t dst_stride,
+                int64_t rows, int64_t cols, int op, int box_rows, int box_cols, int stages,
+                int tiles_per_block, int64_t lds_budget, tp_plan *plan);
 int plan_chunk_copy(uintptr_t src, uintptr_t dst, int64_t n_chunks, uintptr_t pred,
                     uintptr_t src_size, uintptr_t ignore_src, int stages, int tiles_per_block,
                     int64_t lds_budget, tp_plan *plan);
@@ -169,6 +191,9 @@ int launch_map_copy(const tp_plan &plan, const MapParams &p, void *stream);
 int launch_map_split_scale2(const tp_plan &plan, const MapParams &p, void *stream);
 int launch_map_split_horner32(const tp_plan &plan, const MapParams &p, void *stream);
 int launch_map_split_copy(const tp_plan &plan, const MapParams &p, void *stream);
+int launch_map2d_scale2(const tp_plan &plan, const Map2dParams &p, void *stream);
+int launch_map2d_horner32(const tp_plan &plan, const Map2dParams &p, void *stream);
+int launch_map2d_copy(const tp_plan &plan, const Map2dParams &p, void *stream);
 int launch_chunk_copy(const tp_plan &plan, const ChunkParams &p, void *stream);
 
 }  // namespace tp

@@ -1,40 +1,10 @@
 // Software-pipelined tiled map: out[i] = op(in[i]).
 //
-// A workgroup streams its run of `cnt` consecutive tiles through an LDS ring
-// of S slots ("Asynchronous Data Movement", section "Double buffering": the
-// first copy is issued before the loop, and each iteration issues the next
-// stage's copy before waiting on the current one; S slots generalize the two
-// buffers, the "N-buffering" of "CUDA Async Copy and Pipeline Guide", section
-// "Optimization Techniques"). Two schedules, chosen by the load/store widths:
-//
-// Refill-first (loads and stores of the same width). Every lane reads back
-// exactly the bytes it copied itself, so no wave needs another wave's data and
-// the slot a wave has just consumed is free for that wave at once:
-//   prologue   issue tiles 0 .. S-2 into slots 0 .. S-2
-//   iteration t:
-//     issue    tile t+S-1 into slot (t+S-1) mod S = (t-1) mod S   (just consumed)
-//     wait     vmcnt(k_t): this wave's loads of tile t have landed
-//     consume  read tile t from slot t mod S, apply op, store
-// so all S slots are loading while the wave waits for tile t.
-//
-// Exchange (a 16-byte side and a 4-byte side: lanes read bytes other waves
-// copied), the pages' protocol with a workgroup barrier:
-//   prologue   issue tiles 0 .. S-2 into slots 0 .. S-2
-//   iteration t:
-//     wait     vmcnt(k_t): this wave's loads of tile t have landed  (consumer_wait)
-//     barrier  every wave's part of tile t is visible; every wave has finished
-//              reading slot (t-1) mod S in iteration t-1              (consumer_release)
-//     issue    tile t+S-1 into slot (t-1) mod S                       (producer side)
-//     consume  read tile t from slot t mod S, apply op, store
-// so S-1 tiles are in flight while tile t is computed and stored; with S = 1
-// it is the classic load -> barrier -> compute -> barrier ("Asynchronous Data
-// Movement", opening paragraph).
-//
-// Tiles past the end of the workgroup's run are still "issued" as out-of-range
-// loads that move no data: the count of memory instructions between tile t's
-// loads and its wait is then the same for every t, and k_t is a compile-time
-// immediate (the first S-1 iterations, whose loads were issued before any
-// store, are peeled with their own smaller counts).
+// A workgroup streams its run of consecutive tiles through an LDS ring of S
+// slots with the stage loop of tp_pipeline.hpp ("Asynchronous Data Movement",
+// section "Double buffering"); this file supplies what one tile is: where its
+// bytes live in global memory and in its slot, how the lanes split it, and
+// the op applied between the LDS read and the store.
 //
 // Layout: a tile is tile_elems contiguous floats of global memory and sits
 // contiguously in its LDS slot. With the 16-byte path, lane `tid` moves chunk
@@ -48,6 +18,7 @@
 
 #include "tp_engine.hpp"
 #include "tp_internal.hpp"
+#include "tp_pipeline.hpp"
 
 namespace tp {
 namespace dev {
@@ -165,57 +136,8 @@ __global__ void __launch_bounds__(256) map_kernel(MapParams p)
         }
     };
 
-    if (cnt == 0) {
-        // only the final partial chunk (below) is left for this workgroup
-    } else if constexpr (map_wave_local(LX4, SX4)) {
-        static_for<0, S - 1>([&](auto s) TP_INLINE { issue(s, ring + s * tile_bytes); });
-        // Warm-up iterations 0 .. S-2 with their own wait counts (cnt >= 1 here,
-        // so iteration 0 always runs). Every iteration issues before it stores,
-        // so whichever iteration runs last leaves only its stores behind its
-        // final load.
-        static_for<0, S - 1>([&](auto T) TP_INLINE {
-            if ((int)T == 0 || (int)T < cnt) {
-                issue(T + S - 1, ring + ((T + S - 1) % S) * tile_bytes);
-                vm_wait<stage_wait_count(S, LD, ST, T, true)>();
-                consume(T, (T % S) * tile_bytes);
-            }
-        });
-        uint32_t cur = (S - 1) % S;  // slot of tile t
-        for (int t = S - 1; t < cnt; ++t) {
-            const uint32_t nxt = cur == 0 ? S - 1 : cur - 1;  // slot of tile t + S - 1
-            issue(t + S - 1, ring + nxt * tile_bytes);
-            vm_wait<stage_wait_count(S, LD, ST, S - 1, true)>();
-            consume(t, cur * tile_bytes);
-            cur = cur + 1 == S ? 0 : cur + 1;
-        }
-    } else if constexpr (S == 1) {
-        for (int t = 0; t < cnt; ++t) {
-            issue(t, ring);
-            vm_wait<0>();
-            block_sync();
-            consume(t, 0);
-            block_sync();
-        }
-    } else {
-        static_for<0, S - 1>([&](auto s) TP_INLINE { issue(s, ring + s * tile_bytes); });
-        static_for<0, S - 1>([&](auto T) TP_INLINE {
-            if ((int)T == 0 || (int)T < cnt) {    // cnt is uniform: every wave takes the barrier
-                vm_wait<stage_wait_count(S, LD, ST, T)>();
-                block_sync();
-                issue(T + S - 1, ring + ((T + S - 1) % S) * tile_bytes);
-                consume(T, (T % S) * tile_bytes);
-            }
-        });
-        uint32_t cur = (S - 1) % S;  // slot of tile t
-        for (int t = S - 1; t < cnt; ++t) {
-            const uint32_t nxt = cur == 0 ? S - 1 : cur - 1;  // slot of tile t + S - 1
-            vm_wait<stage_wait_count(S, LD, ST, S - 1)>();
-            block_sync();
-            issue(t + S - 1, ring + nxt * tile_bytes);
-            consume(t, cur * tile_bytes);
-            cur = cur + 1 == S ? 0 : cur + 1;
-        }
-    }
+    if (cnt > 0)
+        pipeline_run<S, LD, ST, map_wave_local(LX4, SX4)>(cnt, ring, tile_bytes, issue, consume);
 
     // The final partial 16-byte chunk (n not a multiple of 4): at most three
     // floats, moved element-wise by the first wave of the last workgroup
@@ -231,12 +153,8 @@ __global__ void __launch_bounds__(256) map_kernel(MapParams p)
         MapOp<OP>::apply(v, p.coef);
         store_b32(to, tid * 4, f2u(v[0]));
     }
-    // No copy into LDS may still be in flight when the workgroup's LDS is freed.
-    // Every path ends with one tile's ST stores (or the tail's single store
-    // after a full wait) issued after the last load; operations retire in
-    // issue order, so at most ST outstanding means every load has landed. The
-    // final stores themselves need no wait before the program ends.
-    vm_wait<ST>();
+    // No copy into LDS is in flight here: pipeline_run retires its last load
+    // before it returns, and the tail waits for its own.
 }
 
 // Kernel table of one op: index ((S-1) * 4 + log2 L) * 4 + path.

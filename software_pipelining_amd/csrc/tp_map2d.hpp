@@ -1,0 +1,156 @@
+// Strided 2-D map through the LDS pipeline:
+//   dst[r * dst_stride + c] = op(src[r * src_stride + c]),  r < rows, c < cols.
+//
+// The tile is a box of box_rows x box_cols floats of a row-major matrix,
+// described by a base, a shape and the row strides, as the pages describe a
+// tensor tile transfer ("Asynchronous Data Movement", section "The Tensor
+// Memory Accelerator"). CDNA4 has no engine that walks such a description, so
+// the lanes of the workgroup do it: each lane turns its chunk (or float) of
+// the box into a row and a column and issues an LDS-DMA buffer load from
+// row * stride + column. The box sits in its LDS slot contiguously, row after
+// row, exactly as a 1-D tile of box_rows * box_cols floats does, and the stage
+// loop is the shared one (tp_pipeline.hpp).
+//
+// A workgroup owns a run of tiles_per_block boxes side by side in one band of
+// box_rows rows. Its two buffer descriptors are rebased at the band's first
+// element and cover exactly the band's rows up to the run's last column, so
+// every offset fits 32 bits and an element past the matrix's last row or
+// column, in an edge box, is given the descriptor's first out-of-range offset:
+// its load moves nothing (the LDS gets zeros) and its store is dropped. Every
+// lane still issues the same instructions per box, so the wait counts hold.
+// With 16-byte accesses a chunk never straddles the matrix's last column
+// (cols is a multiple of 4 on that path).
+#pragma once
+
+#include "tp_map.hpp"
+#include "tp_pipeline.hpp"
+
+namespace tp {
+namespace dev {
+
+template <int OP, int S, int L, bool LX4, bool SX4>
+__global__ void __launch_bounds__(256) map2d_kernel(Map2dParams p)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    constexpr int LD = map_loads_per_tile(LX4, L);
+    constexpr int ST = map_stores_per_tile(SX4, L);
+
+    const uint32_t nt = blockDim.x;
+    const uint32_t tid = threadIdx.x;
+    const uint32_t wave_first = uniform(tid & ~63u);
+    const uint32_t tile_bytes = nt * L * 16;
+    const uint32_t bc_log2 = p.box_cols_log2;
+    const uint32_t box_cols = 1u << bc_log2;
+    const uint32_t box_rows = (nt * L * 4) >> bc_log2;
+
+    // This workgroup's run: boxes [first_box, first_box + T) of band `band`.
+    const uint32_t b = blockIdx.x;
+    const uint32_t band = b / p.runs_per_band;
+    const uint32_t first_box = (b - band * p.runs_per_band) * p.tiles_per_block;
+    const int64_t r0 = (int64_t)band * box_rows;
+    const int64_t c0 = (int64_t)first_box * box_cols;
+    const int64_t rows_left = p.rows - r0;
+    const int64_t cols_left = p.cols - c0;
+    const int64_t run_cols = (int64_t)p.tiles_per_block * box_cols;
+    const uint32_t rr = (uint32_t)(rows_left < box_rows ? rows_left : box_rows);    // >= 1
+    const uint32_t cc = (uint32_t)(cols_left < run_cols ? cols_left : run_cols);    // >= 1
+    const int cnt = (int)((cc + box_cols - 1) >> bc_log2);
+    const uint32_t ss = (uint32_t)p.src_stride;
+    const uint32_t ds = (uint32_t)p.dst_stride;
+    const uint32_t src_end = ((rr - 1) * ss + cc) * 4;   // first out-of-range byte
+    const uint32_t dst_end = ((rr - 1) * ds + cc) * 4;
+    const BufferRes rin = make_buffer_res(p.src + r0 * p.src_stride + c0, src_end);
+    const BufferRes rout = make_buffer_res(p.dst + r0 * p.dst_stride + c0, dst_end);
+    const uint32_t ring = uniform(lds_offset(lds));
+
+    // Element e of box j (row-major in the box, 4-aligned on the 16-byte
+    // path): its byte offset in a descriptor with row stride `stride`, or
+    // `end` when it lies outside the matrix.
+    auto elem_offset = [&](uint32_t j, uint32_t e, uint32_t stride, uint32_t end) TP_INLINE {
+        const uint32_t row = e >> bc_log2;
+        const uint32_t col = (j << bc_log2) + (e & (box_cols - 1));
+        return row < rr && col < cc ? (row * stride + col) * 4 : end;
+    };
+
+    auto issue = [&](uint32_t j, uint32_t slot) TP_INLINE {
+        if constexpr (LX4) {
+            static_for<0, L>([&](auto i) TP_INLINE {
+                const uint32_t q = i * nt + tid;   // 16-byte chunk of the box
+                dma_b128(rin, elem_offset(j, q * 4, ss, src_end), uniform(slot + (i * nt + wave_first) * 16));
+            });
+        } else {
+            static_for<0, 4 * L>([&](auto i) TP_INLINE {
+                const uint32_t f = i * nt + tid;   // float of the box
+                dma_b32(rin, elem_offset(j, f, ss, src_end), uniform(slot + (i * nt + wave_first) * 4));
+            });
+        }
+    };
+
+    auto consume = [&](uint32_t j, uint32_t slot_off) TP_INLINE {
+        float v[4 * L];
+        if constexpr (SX4) {
+            static_for<0, L>([&](auto i) TP_INLINE {
+                const f32x4 x = *reinterpret_cast<const f32x4 *>(lds + slot_off + (i * nt + tid) * 16);
+                v[4 * i + 0] = x.x;
+                v[4 * i + 1] = x.y;
+                v[4 * i + 2] = x.z;
+                v[4 * i + 3] = x.w;
+            });
+            MapOp<OP>::apply(v, p.coef);
+            static_for<0, L>([&](auto i) TP_INLINE {
+                const u32x4 o = {f2u(v[4 * i]), f2u(v[4 * i + 1]), f2u(v[4 * i + 2]), f2u(v[4 * i + 3])};
+                store_b128(rout, elem_offset(j, (i * nt + tid) * 4, ds, dst_end), o);
+            });
+        } else {
+            static_for<0, 4 * L>([&](auto i) TP_INLINE {
+                v[i] = *reinterpret_cast<const float *>(lds + slot_off + (i * nt + tid) * 4);
+            });
+            MapOp<OP>::apply(v, p.coef);
+            static_for<0, 4 * L>([&](auto i) TP_INLINE {
+                store_b32(rout, elem_offset(j, i * nt + tid, ds, dst_end), f2u(v[i]));
+            });
+        }
+    };
+
+    pipeline_run<S, LD, ST, map_wave_local(LX4, SX4)>(cnt, ring, tile_bytes, issue, consume);
+}
+
+// Kernel table of one op: index ((S-1) * 4 + log2 L) * 4 + path.
+using Map2dKernelFn = void (*)(Map2dParams);
+
+template <int OP, int I>
+constexpr Map2dKernelFn map2d_entry()
+{
+    constexpr int path = I % 4;
+    constexpr int L = 1 << ((I / 4) % 4);
+    constexpr int S = I / 16 + 1;
+    return &map2d_kernel<OP, S, L, !(path & TP_PATH_SCALAR_LOAD), !(path & TP_PATH_SCALAR_STORE)>;
+}
+
+template <int OP, int... I>
+constexpr std::array<Map2dKernelFn, sizeof...(I)> map2d_table(std::integer_sequence<int, I...>)
+{
+    return {map2d_entry<OP, I>()...};
+}
+
+template <int OP>
+int launch_map2d_op(const tp_plan &plan, const Map2dParams &p, void *stream)
+{
+    static constexpr auto table = map2d_table<OP>(std::make_integer_sequence<int, kMaxStages * 4 * 4>{});
+    const Map2dKernelFn fn = table[map_table_index(plan.stages, plan.lane_chunks, plan.path)];
+    if (plan.lds_bytes > 65536) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 plan.lds_bytes);
+        if (e != hipSuccess)
+            return (int)e;
+    }
+    Map2dParams args = p;
+    void *kargs[] = {&args};
+    return (int)hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3((uint32_t)plan.grid),
+                                dim3((uint32_t)plan.threads), kargs, (size_t)plan.lds_bytes,
+                                (hipStream_t)stream);
+}
+
+}  // namespace dev
+}  // namespace tp

@@ -184,6 +184,92 @@ int plan_map(uintptr_t in, uintptr_t out, int64_t n, int op, int tile_elems, int
     return TP_OK;
 }
 
+void map2d_resolve_box(int64_t cols, int *box_rows, int *box_cols)
+{
+    if (*box_rows != 0 || *box_cols != 0)
+        return;
+    int bc = 4;
+    while (bc < 1024 && bc < cols)
+        bc *= 2;
+    *box_cols = bc;
+    *box_rows = 1024 / bc;
+}
+
+int plan_map_2d(uintptr_t src, int64_t src_stride, uintptr_t dst, int64_t dst_stride,
+                int64_t rows, int64_t cols, int op, int box_rows, int box_cols, int stages,
+                int tiles_per_block, int64_t lds_budget, tp_plan *plan)
+{
+    map2d_resolve_box(cols, &box_rows, &box_cols);
+    if (rows < 0 || cols < 0 || rows > kMaxMapElems || cols > kMaxMapElems)
+        return TP_ERR_INVALID_ARG;
+    if (op != TP_OP_SCALE2 && op != TP_OP_HORNER32 && op != TP_OP_COPY)
+        return TP_ERR_INVALID_ARG;
+    if (stages < 1 || stages > kMaxStages)
+        return TP_ERR_INVALID_ARG;
+    const int64_t tile = (int64_t)box_rows * box_cols;
+    if (box_rows < 1 || box_cols < 4 || (box_rows & (box_rows - 1)) || (box_cols & (box_cols - 1)) ||
+        !valid_tile((int)(tile > 8192 ? 0 : tile)))
+        return TP_ERR_INVALID_ARG;
+    const int tpb = resolve_tiles_per_block(tiles_per_block, kDefaultMapTilesPerBlock);
+    if (tpb < 0)
+        return TP_ERR_INVALID_ARG;
+    const MapGeometry g = map_geometry((int)tile);
+    tp_plan p;
+    memset(&p, 0, sizeof p);
+    p.stages = stages;
+    p.tile_units = (int32_t)tile;
+    p.threads = g.threads;
+    p.lane_chunks = g.lane_chunks;
+    p.tiles_per_block = tpb;
+    p.ring_bytes = (int32_t)(stages * tile * 4);
+    p.schedule = TP_SCHED_UNIFORM;
+    if (p.ring_bytes > lds_budget)
+        return TP_ERR_LDS_BUDGET;
+    p.lds_bytes = p.ring_bytes;
+    p.path = TP_PATH_X4;
+    if (rows > 0 && cols > 0) {
+        if (!src || !dst)
+            return TP_ERR_INVALID_ARG;
+        if (src % 4 || dst % 4)
+            return TP_ERR_MISALIGNED;
+        if (src_stride < cols || dst_stride < cols || src_stride > kMaxStride ||
+            dst_stride > kMaxStride)
+            return TP_ERR_INVALID_ARG;
+        // one workgroup's band, up to its run's last column, stays well inside
+        // 32-bit buffer offsets on both sides
+        const int64_t run_cols = (int64_t)tpb * box_cols;
+        if (((box_rows - 1) * src_stride + run_cols) * 4 > kMaxRunBytes ||
+            ((box_rows - 1) * dst_stride + run_cols) * 4 > kMaxRunBytes)
+            return TP_ERR_INVALID_ARG;
+        const uint64_t src_bytes = (uint64_t)((rows - 1) * src_stride + cols) * 4;
+        const uint64_t dst_bytes = (uint64_t)((rows - 1) * dst_stride + cols) * 4;
+        if (!(src == dst && src_stride == dst_stride) && overlaps(src, src_bytes, dst, dst_bytes))
+            return TP_ERR_OVERLAP;
+        const int64_t bands = ceil_div(rows, box_rows);
+        const int64_t boxes_per_band = ceil_div(cols, box_cols);
+        const int64_t runs = ceil_div(boxes_per_band, tpb);
+        if (bands * runs > INT32_MAX)
+            return TP_ERR_INVALID_ARG;
+        p.num_tiles = bands * boxes_per_band;
+        p.grid = bands * runs;
+        const bool load_x4 = src % 16 == 0 && src_stride % 4 == 0 && cols % 4 == 0;
+        const bool store_x4 = dst % 16 == 0 && dst_stride % 4 == 0 && cols % 4 == 0;
+        p.path = (load_x4 ? 0 : TP_PATH_SCALAR_LOAD) | (store_x4 ? 0 : TP_PATH_SCALAR_STORE);
+    }
+    const bool load_x4 = !(p.path & TP_PATH_SCALAR_LOAD);
+    const bool store_x4 = !(p.path & TP_PATH_SCALAR_STORE);
+    p.wait_steady = stage_wait_count(stages, map_loads_per_tile(load_x4, g.lane_chunks),
+                                     map_stores_per_tile(store_x4, g.lane_chunks), stages,
+                                     map_wave_local(load_x4, store_x4));
+    const int cap = map_policy_resident_cap(op, (int)tile, stages, tpb, g.threads / 64);
+    p.resident_cap = cap;
+    if (cap)
+        p.lds_bytes = reserve_for_cap(p.ring_bytes, cap, lds_budget);
+    if (plan)
+        *plan = p;
+    return TP_OK;
+}
+
 int plan_chunk_copy(uintptr_t src, uintptr_t dst, int64_t n_chunks, uintptr_t pred,
                     uintptr_t src_size, uintptr_t ignore_src, int stages, int tiles_per_block,
                     int64_t lds_budget, tp_plan *plan)

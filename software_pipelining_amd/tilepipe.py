@@ -113,6 +113,8 @@ def _load():
         "tp_plan_row_shift": ([vp, vp, i64, i64, pp], i32),
         "tp_plan_pipelined_map": ([vp, vp, i64, i32, i32, i32, i32, i32, i32, i64, pp], i32),
         "tp_plan_chunk_copy": ([vp, vp, i64, vp, vp, vp, i32, i32, i64, pp], i32),
+        "tp_map_2d": ([vp, i64, vp, i64, i64, i64, i32, i32, i32, i32, i32, vp, ip], i32),
+        "tp_plan_map_2d": ([vp, i64, vp, i64, i64, i64, i32, i32, i32, i32, i32, i64, pp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -217,6 +219,40 @@ def pipelined_map(x, y=None, op: str = "scale2", tile_elems: int = 1024, stages:
     return Path(path.value)
 
 
+def _row_stride(t, name: str) -> int:
+    """Elements between the rows of a 2-D float32 view with unit column stride."""
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D view")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride")
+    return t.stride(0) if t.shape[0] > 1 else max(1, t.shape[1])   # one row: any stride will do
+
+
+def map_2d(src, dst, op: str = "scale2", box_rows: int = 0, box_cols: int = 0,
+           stages: int = 2, boxes_per_block: int = 0, stream=None) -> Path:
+    """dst[r, c] = op(src[r, c]) for two same-shape 2-D float32 GPU views with
+    unit column stride (rows any number of elements apart). box 0 x 0: the
+    library's choice (1024 floats, as wide as the window allows)."""
+    import torch
+    if op not in OPS:
+        raise ValueError(f"unknown op {op!r}; expected one of {sorted(OPS)}")
+    for t, name in ((src, "src"), (dst, "dst")):
+        if t.dtype != torch.float32 or not t.is_cuda:
+            raise TypeError(f"{name} must be a float32 CUDA tensor")
+    if tuple(src.shape) != tuple(dst.shape):
+        raise ValueError("src and dst must have the same shape")
+    _same_device(src, dst)
+    rows, cols = src.shape
+    path = ctypes.c_int(0)
+    with torch.cuda.device(src.device):
+        st = _load().tp_map_2d(ctypes.c_void_p(src.data_ptr()), _row_stride(src, "src"),
+                               ctypes.c_void_p(dst.data_ptr()), _row_stride(dst, "dst"),
+                               rows, cols, OPS[op], box_rows, box_cols, stages, boxes_per_block,
+                               _stream_handle(src, stream), ctypes.byref(path))
+    _check(st, "tp_map_2d")
+    return Path(path.value)
+
+
 def chunk_copy(src, dst, pred=None, src_size=None, ignore_src=None, stages: int = 2,
                tiles_per_block: int = 0, stream=None) -> Path:
     """Predicated copy of 16-byte chunks: src/dst are uint8 GPU tensors of
@@ -273,6 +309,17 @@ def plan_map(in_ptr: int, out_ptr: int, n: int, op: str = "scale2", tile_elems: 
                                        tile_elems, stages, tiles_per_block, resident_cap,
                                        _schedule(schedule), lds_budget, ctypes.byref(cp))
     return _plan(st, cp, "tp_plan_pipelined_map")
+
+
+def plan_map_2d(src_ptr: int, src_stride: int, dst_ptr: int, dst_stride: int, rows: int,
+                cols: int, op: str = "scale2", box_rows: int = 0, box_cols: int = 0,
+                stages: int = 2, boxes_per_block: int = 0, lds_budget: int = _NO_BUDGET) -> Plan:
+    cp = _CPlan()
+    st = _load().tp_plan_map_2d(ctypes.c_void_p(src_ptr), src_stride, ctypes.c_void_p(dst_ptr),
+                                dst_stride, rows, cols,
+                                OPS.get(op, op if isinstance(op, int) else -1), box_rows,
+                                box_cols, stages, boxes_per_block, lds_budget, ctypes.byref(cp))
+    return _plan(st, cp, "tp_plan_map_2d")
 
 
 def plan_chunk_copy(src_ptr: int, dst_ptr: int, n_chunks: int, pred_ptr: int = 0,

@@ -236,6 +236,88 @@ def test_map_role_split_plan():
     assert _status(tp.plan_map, A, B, 10, "scale2", 1024, 2, 2, tilepipe._NO_BUDGET, 0, -1) == 1
 
 
+# ------------------------------------------------------------------ 2-D map
+def test_map_2d_plan_geometry_and_paths():
+    p = tp.plan_map_2d(A, 1000, B, 1024, 100, 1000, "scale2", 4, 256, 2, 3)
+    assert (p.tile_units, p.threads, p.lane_chunks, p.tiles_per_block) == (1024, 256, 1, 3)
+    bands, boxes = -(-100 // 4), -(-1000 // 256)
+    assert (p.num_tiles, p.grid) == (bands * boxes, bands * -(-boxes // 3))
+    assert p.ring_bytes == 2 * 1024 * 4 and p.lds_bytes >= p.ring_bytes
+    assert p.path == tp.Path.X4
+    assert tp.plan_map_2d(A + 4, 1000, B, 1024, 100, 1000).path == tp.Path.SCALAR_LOAD
+    assert tp.plan_map_2d(A, 1002, B, 1024, 100, 1000).path == tp.Path.SCALAR_LOAD   # stride
+    assert tp.plan_map_2d(A, 1000, B, 1026, 100, 1000).path == tp.Path.SCALAR_STORE
+    assert tp.plan_map_2d(A, 1000, B, 1024, 100, 998).path == tp.Path.SCALAR          # cols
+    for br, bc, threads, lanes in [(1, 256, 64, 1), (64, 4, 64, 1), (2, 4096, 256, 8), (16, 64, 256, 1)]:
+        p = tp.plan_map_2d(A, 8192, B, 8192, 50, 5000, "copy", br, bc, 1, 1)
+        assert (p.threads, p.lane_chunks) == (threads, lanes)
+    # nothing to do: no launch, null pointers accepted
+    assert tp.plan_map_2d(0, 0, 0, 0, 0, 10).grid == 0
+    assert tp.plan_map_2d(0, 0, 0, 0, 10, 0).grid == 0
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, 100, B, 100, 10, 100, "scale2", 4, 2), 1),        # box_cols < 4
+    ((A, 100, B, 100, 10, 100, "scale2", 0, 256), 1),      # only one side of the box given
+    ((A, 100, B, 100, 10, 100, "scale2", 3, 256), 1),      # box_rows not a power of two
+    ((A, 100, B, 100, 10, 100, "scale2", 4, 32), 1),       # box of 128 floats
+    ((A, 100, B, 100, 10, 100, "scale2", 4, 4096), 1),     # box of 16384 floats
+    ((A, 99, B, 100, 10, 100), 1),                         # stride < cols
+    ((A, 100, B, 100, 10, 100, "nope"), 1),
+    ((A, 100, B, 100, -1, 100), 1),
+    ((A, 1 << 37, B, 100, 10, 100), 1),                    # stride too large
+    ((A, 1 << 20, B, 100, 10, 100, "scale2", 512, 4), 1),  # a band spans more than 1 GiB
+    ((A + 2, 100, B, 100, 10, 100), 2),
+    ((A, 100, B + 1, 100, 10, 100), 2),
+    ((A, 100, A + 400, 100, 10, 100), 4),                  # dst window inside src's range
+    ((A, 100, A, 200, 10, 100), 4),                        # same base, other stride
+    ((0, 100, B, 100, 10, 100), 1),
+])
+def test_map_2d_plan_errors(args, status):
+    assert _status(tp.plan_map_2d, *args) == status
+
+
+def test_map_2d_workgroup_windows_stay_inside_the_matrix():
+    # Each workgroup of the 2-D kernel rebases its two buffer descriptors at its
+    # band and run: base = r0 * stride + c0, num_records = ((rr - 1) * stride + cc) * 4,
+    # with band = b / runs_per_band, r0 = band * box_rows, c0 = first box * box_cols.
+    # Every access is range-checked against that window, so the window lying
+    # inside the caller's matrix (and in 32 bits) bounds every access.
+    for rows, cols, ss, br, bc, T in [(1, 1, 1, 1, 256, 2), (5, 3, 7, 64, 4, 1), (100, 1000, 1003, 4, 256, 3),
+                                      (257, 64, 64, 16, 64, 2), (3, 9000, 9000, 1, 8192, 1),
+                                      (1000, 5, 8, 2, 128, 65536), (37, 37, 40, 8, 32, 5)]:
+        p = tp.plan_map_2d(A, ss, B, ss, rows, cols, "copy", br, bc, 1, T)
+        runs = -(-(-(-cols // bc)) // p.tiles_per_block)
+        extent = (rows - 1) * ss + cols
+        assert p.grid == -(-rows // br) * runs
+        for b in range(p.grid):
+            band, first_box = b // runs, (b % runs) * p.tiles_per_block
+            r0, c0 = band * br, first_box * bc
+            rr, cc = min(br, rows - r0), min(p.tiles_per_block * bc, cols - c0)
+            assert rr >= 1 and cc >= 1, (rows, cols, b)
+            base, n = r0 * ss + c0, (rr - 1) * ss + cc
+            assert 0 <= base and base + n <= extent and n * 4 < 1 << 32, (rows, cols, b)
+
+
+def test_map_2d_default_box():
+    # 0 x 0: 1024-float boxes, as wide as the window allows
+    for cols, units in [(1, 1024), (4, 1024), (5, 1024), (300, 1024), (1024, 1024), (16384, 1024)]:
+        assert tp.plan_map_2d(A, 20000, B, 20000, 10, cols).tile_units == units
+    p = tp.plan_map_2d(A, 16448, B, 16384, 16384, 16384)
+    assert p.grid == 16384 * (16 // 2)              # 1 x 1024 boxes, runs of 2
+    p = tp.plan_map_2d(A, 64, B, 64, 1000, 64)
+    assert p.grid == -(-1000 // 16)                 # 16 x 64 boxes: one run per band
+    assert _status(tp.plan_map_2d, A, 100, B, 100, 10, 100, "scale2", 0, 256) == 1
+
+
+def test_map_2d_plan_in_place_and_budget():
+    assert tp.plan_map_2d(A, 100, A, 100, 10, 100).grid > 0          # exact aliasing is allowed
+    assert _status(tp.plan_map_2d, A, 100, B, 100, 10, 100, "scale2", 4, 2048, 8, 0,
+                   160 * KIB) == 3                                   # 8 x 32 KiB of ring
+    p = tp.plan_map_2d(A, 100, B, 100, 10, 100, "horner32", 1, 256, 2, 2)
+    assert (p.resident_cap, p.lds_bytes) == (0, p.ring_bytes)       # horner32: not bounded
+
+
 # ------------------------------------------------------------ row shift
 def test_row_shift_plan():
     p = tp.plan_row_shift(A, B, 64)
