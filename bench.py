@@ -41,10 +41,12 @@ def parse():
     ap.add_argument("--tiles-per-block", type=int, default=0,
                     help="consecutive tiles per workgroup (0: the library default)")
     ap.add_argument("--quick", action="store_true", help="headline only: no sweep, no extra rows")
-    ap.add_argument("--mode", choices=("bench", "stages", "sweep", "occupancy"), default="bench",
+    ap.add_argument("--mode", choices=("bench", "stages", "sweep", "occupancy", "map2d"),
+                    default="bench",
                     help="stages: only the maps at 1-4 stages; sweep: only the 24-point stage/tile "
                          "sweep (both for hardware-counter passes); occupancy: scale2 bandwidth "
-                         "against the bound on resident workgroups per CU")
+                         "against the bound on resident workgroups per CU; map2d: only the 2-D "
+                         "map with its default box (for counter passes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline")
@@ -234,6 +236,27 @@ def sweep_mode(args):
     torch.cuda.synchronize()
 
 
+def map2d_mode(args):
+    """The 2-D map workload with the library's default box, `steps` times, plus
+    the runtime's 1 GiB copy for the traffic counters' calibration."""
+    import torch
+    import software_pipelining_amd as tp
+    dev = torch.device("cuda:0")
+    R, C, SS = MAP2D_ROWS, MAP2D_COLS, MAP2D_SRC_STRIDE
+    src = torch.empty(R, SS, device=dev).uniform_(-1, 1)[:, :C]
+    dst = torch.empty(R, C, device=dev)
+    f = lambda: tp.map_2d(src, dst, "scale2")
+    gpu_warmup(f)
+    per, _ = time_launches(f, 1, args.steps)
+    log(f"map_2d {R}x{C} (row stride {SS}), default box: {median(per) * 1e3:.1f} us, "
+        f"{8 * R * C / (median(per) * 1e-3) / 1e9:.0f} GB/s")
+    flat = torch.empty(1 << 28, device=dev)
+    out = torch.empty_like(flat)
+    for _ in range(3):
+        out.copy_(flat)
+    torch.cuda.synchronize()
+
+
 def occupancy_mode(args):
     """scale2 over 2^28 at tiles 256/1024/4096, runs of 2/4/8, 1/2/4 stages:
     bandwidth with no bound on resident workgroups, with the library's bound,
@@ -285,6 +308,9 @@ def main():
         return
     if args.mode == "occupancy":
         occupancy_mode(args)
+        return
+    if args.mode == "map2d":
+        map2d_mode(args)
         return
 
     import numpy as np
