@@ -318,6 +318,28 @@ def test_map_2d_plan_in_place_and_budget():
     assert (p.resident_cap, p.lds_bytes) == (0, p.ring_bytes)       # horner32: not bounded
 
 
+# ------------------------------------------------- binding argument checks
+def test_binding_rejects_bad_tensors_before_the_library():
+    import torch
+    x = torch.zeros(16)
+    with pytest.raises(ValueError):
+        tp.pipelined_map(x, x.clone())                         # a CPU tensor: no CPU path
+    with pytest.raises(ValueError):
+        tp.pipelined_map(x, x.clone(), "cube")                 # unknown op
+    with pytest.raises(ValueError):
+        tilepipe._schedule("eager")
+    assert tilepipe._schedule("role_split") == tp.Schedule.ROLE_SPLIT
+    assert tilepipe._schedule(7) == 7                          # passed through; the library decides
+    with pytest.raises(TypeError):
+        tp.map_2d(x.view(4, 4), x.view(4, 4).clone())         # not CUDA tensors
+    with pytest.raises(ValueError):
+        tp.map_2d(x.view(4, 4), x.view(2, 8), "cube")
+    with pytest.raises(ValueError):
+        tp.row_shift(x.view(4, 4))                             # a CPU tensor
+    with pytest.raises(ValueError):
+        tilepipe._row_stride(x.view(4, 4).t(), "src")          # column stride 4
+
+
 # ------------------------------------------------------------ row shift
 def test_row_shift_plan():
     p = tp.plan_row_shift(A, B, 64)
