@@ -533,9 +533,10 @@ def extra_rows(args, tp, workloads, torch, np, dev, x_host, xbuf, y):
 
     rows["map_2d"] = map_2d_row(tp, workloads, torch, np, dev, y)
 
-    # predicated chunk copy: 2^26 chunks. Not timed on the GPU in this test
-    # window (it faulted twice before its wait-state hazard was found and fixed).
-    rows["chunk_copy"] = {"n_chunks": 1 << 26, "status": "not run on the GPU in this test window"}
+    # predicated chunk copy: 2^26 chunks. Not timed: it is kept off the GPU
+    # until the fix of its wait-state hazard has had its GPU run.
+    rows["chunk_copy"] = {"n_chunks": 1 << 26,
+                          "status": "not run: kept off the GPU until its hazard fix is tested"}
 
     # row exchange 64x4 (launch-bound)
     a = workloads.arange_rows(64).to(dev)

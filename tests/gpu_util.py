@@ -10,10 +10,11 @@ import torch
 # inline-asm buffer instructions, which then read stale SGPRs (a VALU-written
 # SGPR needs 5 wait states before a vector-memory instruction reads it). The
 # asm blocks now carry those wait states and a static check of the built code
-# object enforces them (test_isa_hazards.py), but a case that faulted after a
-# first fix stays off the GPU until the next test window.
-CHUNK_COPY_GPU_SKIP = ("chunk copy kept off the GPU this test window: it faulted twice before the "
-                       "descriptor wait-state hazard was found and fixed")
+# object enforces them (test_isa_hazards.py). A case that faulted again after
+# a first fix is kept off the GPU until the fix of its shown cause gets its own
+# GPU run.
+CHUNK_COPY_GPU_SKIP = ("chunk copy kept off the GPU: it faulted twice before the descriptor "
+                       "wait-state hazard was found and fixed, and that fix has not had its GPU run")
 
 GUARD = 64                      # sentinel words before and after every buffer
 SENTINEL = 0x7FC0DEAD           # a NaN pattern none of the tests' results contain
