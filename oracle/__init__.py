@@ -57,6 +57,8 @@ def _load():
     lib.oracle_horner32_subnormal_steps.restype = i64
     lib.oracle_chunk_copy.argtypes = [p, p, p, p, p, i64, i64]
     lib.oracle_chunk_copy.restype = None
+    lib.oracle_chunk_copy_w.argtypes = [p, p, ctypes.c_int, p, p, p, i64, i64]
+    lib.oracle_chunk_copy_w.restype = None
     lib.oracle_map_2d.argtypes = [p, i64, p, i64, i64, ctypes.c_int, i64, i64]
     lib.oracle_map_2d.restype = None
     _lib = lib
@@ -179,17 +181,20 @@ def horner32_subnormal_steps(x: np.ndarray, threads: int | None = None) -> int:
 # --------------------------------------------------------------- chunk copy
 def chunk_copy(src: np.ndarray, dst: np.ndarray, pred: np.ndarray | None = None,
                src_size: np.ndarray | None = None, ignore_src: np.ndarray | None = None,
-               threads: int | None = None) -> np.ndarray:
-    """Return a new array: dst after the predicated 16-byte chunk copy.
+               threads: int | None = None, chunk_bytes: int = 16) -> np.ndarray:
+    """Return a new array: dst after the predicated chunk copy.
 
-    src and dst are uint8 arrays of n_chunks * 16 bytes (any shape); the
-    metadata arrays are uint8 of n_chunks, or None for their defaults.
+    src and dst are uint8 arrays of n_chunks * chunk_bytes bytes (any shape),
+    chunk_bytes 4, 8 or 16; the metadata arrays are uint8 of n_chunks, or None
+    for their defaults.
     """
+    if chunk_bytes not in (4, 8, 16):
+        raise ValueError("chunk_bytes must be 4, 8 or 16")
     src = _contig(src.reshape(-1), np.uint8)
     res = np.array(dst.reshape(-1), dtype=np.uint8, copy=True)
-    if src.size != res.size or src.size % 16:
-        raise ValueError("src and dst must hold the same whole number of 16-byte chunks")
-    n = src.size // 16
+    if src.size != res.size or src.size % chunk_bytes:
+        raise ValueError(f"src and dst must hold the same whole number of {chunk_bytes}-byte chunks")
+    n = src.size // chunk_bytes
     meta = []
     for m in (pred, src_size, ignore_src):
         if m is not None:
@@ -197,7 +202,7 @@ def chunk_copy(src: np.ndarray, dst: np.ndarray, pred: np.ndarray | None = None,
             if m.size != n:
                 raise ValueError("metadata arrays need one byte per chunk")
         meta.append(m)
-    _run_ranged(_load().oracle_chunk_copy,
-                (_ptr(src), _ptr(res), *(_ptr(m) for m in meta)), n,
+    _run_ranged(_load().oracle_chunk_copy_w,
+                (_ptr(src), _ptr(res), chunk_bytes, *(_ptr(m) for m in meta)), n,
                 threads or default_threads())
     return res.reshape(dst.shape)

@@ -143,35 +143,45 @@ int64_t oracle_horner32_subnormal_steps(const float *in, int64_t lo, int64_t hi)
 }
 
 /*
- * Predicated 16-byte chunk copy ("Asynchronous Copies", section "A
- * Global-to-Shared Copy", the paragraph on the copy's optional operands):
+ * Predicated chunk copy ("Asynchronous Copies", section "A Global-to-Shared
+ * Copy", the paragraph on the copy's optional operands), for chunks of
+ * `width` = 4, 8 or 16 bytes, the element sizes the pages name for the fast
+ * copy path ("Asynchronous Data Movement", section "Alignment requirements"):
  *   - a false predicate skips the copy and leaves the destination chunk as it
  *     was (it is not written at all);
  *   - otherwise, ignore_src set: the whole chunk becomes zero bytes;
- *   - otherwise, the first s = min(src_size, 16) bytes come from the source
- *     chunk and the remaining 16 - s bytes become zero.
+ *   - otherwise, the first s = min(src_size, width) bytes come from the source
+ *     chunk and the remaining width - s bytes become zero.
  * pred and ignore_src are bytes read as nonzero = true. A NULL array means its
- * default for every chunk: pred all true, src_size all 16, ignore_src all
- * false. src and dst hold 16 bytes per chunk; they may be the same buffer
- * (every chunk is computed from its own source bytes only).
+ * default for every chunk: pred all true, src_size all `width`, ignore_src all
+ * false. src and dst hold `width` bytes per chunk; they may be the same
+ * buffer (every chunk is computed from its own source bytes only).
+ * oracle_chunk_copy is the 16-byte case.
  */
-void oracle_chunk_copy(const uint8_t *src, uint8_t *dst,
-                       const uint8_t *pred, const uint8_t *src_size,
-                       const uint8_t *ignore_src, int64_t lo, int64_t hi)
+void oracle_chunk_copy_w(const uint8_t *src, uint8_t *dst, int width,
+                         const uint8_t *pred, const uint8_t *src_size,
+                         const uint8_t *ignore_src, int64_t lo, int64_t hi)
 {
     for (int64_t i = lo; i < hi; ++i) {
         const int p = pred ? (pred[i] != 0) : 1;
         if (!p)
             continue;
         const int ign = ignore_src ? (ignore_src[i] != 0) : 0;
-        int s = src_size ? (int)src_size[i] : 16;
-        if (s > 16)
-            s = 16;
+        int s = src_size ? (int)src_size[i] : width;
+        if (s > width)
+            s = width;
         if (ign)
             s = 0;
         uint8_t chunk[16];
-        for (int b = 0; b < 16; ++b)
-            chunk[b] = (b < s) ? src[16 * i + b] : 0;
-        memcpy(dst + 16 * i, chunk, 16);
+        for (int b = 0; b < width; ++b)
+            chunk[b] = (b < s) ? src[(int64_t)width * i + b] : 0;
+        memcpy(dst + (int64_t)width * i, chunk, (size_t)width);
     }
+}
+
+void oracle_chunk_copy(const uint8_t *src, uint8_t *dst,
+                       const uint8_t *pred, const uint8_t *src_size,
+                       const uint8_t *ignore_src, int64_t lo, int64_t hi)
+{
+    oracle_chunk_copy_w(src, dst, 16, pred, src_size, ignore_src, lo, hi);
 }

@@ -283,28 +283,56 @@ def test_chunk_copy_golden_rules():
         assert out[k].tobytes() == c[5], k
 
 
-def test_chunk_copy_brute_force_all_operand_combinations():
+@pytest.mark.parametrize("width", [4, 8, 16])
+def test_chunk_copy_brute_force_all_operand_combinations(width):
     pred_vals = [0, 1, 7, 255]
     ign_vals = [0, 1, 200]
     size_vals = list(range(17)) + [17, 100, 255]
     combos = [(p, g, s) for p in pred_vals for g in ign_vals for s in size_vals]
     n = len(combos)
-    rng = np.random.default_rng(3)
-    src = rng.integers(1, 256, size=(n, 16), dtype=np.uint8)     # no zero bytes
-    dst = rng.integers(1, 256, size=(n, 16), dtype=np.uint8)
+    rng = np.random.default_rng(3 + width)
+    src = rng.integers(1, 256, size=(n, width), dtype=np.uint8)     # no zero bytes
+    dst = rng.integers(1, 256, size=(n, width), dtype=np.uint8)
     pred = np.array([c[0] for c in combos], np.uint8)
     ign = np.array([c[1] for c in combos], np.uint8)
     size = np.array([c[2] for c in combos], np.uint8)
-    out = oracle.chunk_copy(src, dst, pred, size, ign).reshape(n, 16)
+    out = oracle.chunk_copy(src, dst, pred, size, ign, chunk_bytes=width).reshape(n, width)
     for k, (p, g, s) in enumerate(combos):
         if p == 0:
             expect = dst[k]
         elif g != 0:
-            expect = np.zeros(16, np.uint8)
+            expect = np.zeros(width, np.uint8)
         else:
-            m = min(s, 16)
-            expect = np.concatenate([src[k, :m], np.zeros(16 - m, np.uint8)])
-        assert np.array_equal(out[k], expect), (p, g, s)
+            m = min(s, width)
+            expect = np.concatenate([src[k, :m], np.zeros(width - m, np.uint8)])
+        assert np.array_equal(out[k], expect), (width, p, g, s)
+
+
+@pytest.mark.parametrize("width", [4, 8])
+def test_chunk_copy_narrow_widths_special_cases(width):
+    rng = np.random.default_rng(width)
+    n = 5000
+    src = rng.integers(0, 256, size=(n, width), dtype=np.uint8)
+    dst = rng.integers(0, 256, size=(n, width), dtype=np.uint8)
+    zeros, ones = np.zeros(n, np.uint8), np.ones(n, np.uint8)
+    cc = lambda *m: oracle.chunk_copy(src, dst, *m, chunk_bytes=width)
+    assert np.array_equal(cc(zeros, None, ones), dst)                       # all pred false
+    assert np.array_equal(cc(None, None, None), src)                         # defaults: copy
+    assert np.array_equal(cc(ones, np.full(n, width, np.uint8), zeros), src)
+    assert not cc(None, zeros, None).any() and not cc(None, None, ones).any()
+    # a chunk of `width` bytes equals the first `width` bytes of the 16-byte
+    # chunk with the same operands and src_size capped at `width`
+    size = rng.integers(0, 20, size=n).astype(np.uint8)
+    pred = rng.integers(0, 2, size=n).astype(np.uint8)
+    ign = (rng.random(n) < 0.1).astype(np.uint8)
+    wide_src = np.zeros((n, 16), np.uint8)
+    wide_src[:, :width] = src
+    wide_dst = np.zeros((n, 16), np.uint8)
+    wide_dst[:, :width] = dst
+    wide = oracle.chunk_copy(wide_src, wide_dst, pred, np.minimum(size, width).astype(np.uint8), ign)
+    assert np.array_equal(cc(pred, size, ign), wide[:, :width])
+    with pytest.raises(ValueError):
+        oracle.chunk_copy(src, dst, chunk_bytes=12)
 
 
 def test_chunk_copy_special_cases_and_defaults():
