@@ -96,6 +96,7 @@ typedef struct tp_plan {
     int32_t resident_cap;    /* about this many workgroups per CU (0: hardware limits only);
                                 lds_bytes is padded up to bound residency */
     int32_t schedule;        /* tp_schedule (map); 0 for the other entry points */
+    int32_t chunk_bytes;     /* bytes per chunk (chunk copy); 0 for the other entry points */
 } tp_plan;
 
 /* Human-readable name of a tp_status value ("TP_OK", ...); never NULL. */
@@ -237,6 +238,21 @@ TP_API int tp_chunk_copy(const void *src, void *dst, int64_t n_chunks,
                          void *stream, int *path_out);
 
 /*
+ * tp_chunk_copy for chunks of chunk_bytes = 4, 8 or 16 bytes (tp_chunk_copy is
+ * chunk_bytes 16), the element sizes the pages name for the fast copy path
+ * ("Asynchronous Data Movement", section "Alignment requirements"). The
+ * operands keep their meaning with 16 replaced by chunk_bytes: s =
+ * min(src_size[i], chunk_bytes) bytes are copied and the rest of the chunk is
+ * zeroed. src and dst hold n_chunks x chunk_bytes bytes, 4-byte aligned; 4-
+ * and 8-byte chunks always move as 4-byte words (path_out TP_PATH_SCALAR).
+ * Other chunk_bytes: TP_ERR_INVALID_ARG.
+ */
+TP_API int tp_chunk_copy_ex(const void *src, void *dst, int64_t n_chunks, int chunk_bytes,
+                            const uint8_t *pred, const uint8_t *src_size,
+                            const uint8_t *ignore_src, int stages, int tiles_per_block,
+                            void *stream, int *path_out);
+
+/*
  * Host-only planning: the same validation and launch plan as the entry point
  * of the same name, for the given pointer values and LDS budget (bytes per
  * workgroup), without touching any device. Pointers are only inspected for
@@ -254,7 +270,7 @@ TP_API int tp_plan_map_2d(const void *src, int64_t src_stride, const void *dst,
                           int box_cols, int stages, int boxes_per_block, int64_t lds_budget,
                           tp_plan *plan);
 TP_API int tp_plan_chunk_copy(const void *src, const void *dst, int64_t n_chunks,
-                              const void *pred, const void *src_size,
+                              int chunk_bytes, const void *pred, const void *src_size,
                               const void *ignore_src, int stages, int tiles_per_block,
                               int64_t lds_budget, tp_plan *plan);
 

@@ -142,12 +142,13 @@ TP_API int tp_plan_map_2d(const void *src, int64_t src_stride, const void *dst,
 }
 
 TP_API int tp_plan_chunk_copy(const void *src, const void *dst, int64_t n_chunks,
-                              const void *pred, const void *src_size, const void *ignore_src,
-                              int stages, int tiles_per_block, int64_t lds_budget, tp_plan *plan)
+                              int chunk_bytes, const void *pred, const void *src_size,
+                              const void *ignore_src, int stages, int tiles_per_block,
+                              int64_t lds_budget, tp_plan *plan)
 {
-    return tp::plan_chunk_copy((uintptr_t)src, (uintptr_t)dst, n_chunks, (uintptr_t)pred,
-                               (uintptr_t)src_size, (uintptr_t)ignore_src, stages,
-                               tiles_per_block, lds_budget, plan);
+    return tp::plan_chunk_copy((uintptr_t)src, (uintptr_t)dst, n_chunks, chunk_bytes,
+                               (uintptr_t)pred, (uintptr_t)src_size, (uintptr_t)ignore_src,
+                               stages, tiles_per_block, lds_budget, plan);
 }
 
 TP_API int tp_row_shift(const float *a, float *b, int64_t rows, void *stream, int *path_out)
@@ -273,10 +274,19 @@ TP_API int tp_chunk_copy(const void *src, void *dst, int64_t n_chunks, const uin
                          const uint8_t *src_size, const uint8_t *ignore_src, int stages,
                          int tiles_per_block, void *stream, int *path_out)
 {
+    return tp_chunk_copy_ex(src, dst, n_chunks, 16, pred, src_size, ignore_src, stages,
+                            tiles_per_block, stream, path_out);
+}
+
+TP_API int tp_chunk_copy_ex(const void *src, void *dst, int64_t n_chunks, int chunk_bytes,
+                            const uint8_t *pred, const uint8_t *src_size,
+                            const uint8_t *ignore_src, int stages, int tiles_per_block,
+                            void *stream, int *path_out)
+{
     tp_plan plan;
-    int st = tp::plan_chunk_copy((uintptr_t)src, (uintptr_t)dst, n_chunks, (uintptr_t)pred,
-                                 (uintptr_t)src_size, (uintptr_t)ignore_src, stages,
-                                 tiles_per_block, kNoBudget, &plan);
+    int st = tp::plan_chunk_copy((uintptr_t)src, (uintptr_t)dst, n_chunks, chunk_bytes,
+                                 (uintptr_t)pred, (uintptr_t)src_size, (uintptr_t)ignore_src,
+                                 stages, tiles_per_block, kNoBudget, &plan);
     if (st != TP_OK)
         return st;
     if (path_out)

@@ -1,4 +1,5 @@
-// Predicated 16-byte chunk copy through the LDS copy pipeline.
+// Predicated chunk copy through the LDS copy pipeline, for chunks of W = 16
+// bytes and, with the same schedule, W = 8 and 4 bytes.
 //
 // Semantics ("Asynchronous Copies", section "A Global-to-Shared Copy", the
 // paragraph on the copy's operands): a false pred skips the copy and leaves
@@ -11,10 +12,12 @@
 //
 // One lane owns one chunk of a 256-chunk tile. Per tile, each wave issues
 //   three 1-byte LDS-DMA loads (pred, src_size, ignore_src of its 64 chunks)
-//   one 16-byte LDS-DMA load of its 64 chunks (four 4-byte loads on the
-//   fallback path for a source that is not 16-byte aligned)
+//   one 16-byte LDS-DMA load of its 64 chunks (W = 16 with a 16-byte-aligned
+//   source), or else W/4 4-byte loads covering the wave's 64 * W bytes, word
+//   after word, so every chunk lands contiguously at LDS byte tid * W
 // and on consumption reads its chunk and the three bytes back from LDS,
-// zeroes the bytes past the prefix and stores 16 bytes (or four words), with
+// zeroes the bytes past the prefix and stores W bytes (one 16-byte store or
+// W/4 words), with
 // the store's offset out of range when pred is false, so the destination is
 // never written there. Everything a lane reads from LDS was loaded by its own
 // wave, so the per-wave vmcnt wait is the whole synchronization; no workgroup
@@ -36,14 +39,16 @@
 namespace tp {
 namespace dev {
 
-template <int S, bool LX4, bool SX4>
+template <int S, int W, bool LX4, bool SX4>
 __global__ void __launch_bounds__(256) chunk_copy_kernel(ChunkParams p)
 {
+    static_assert(W == 16 || ((W == 8 || W == 4) && !LX4 && !SX4), "narrow chunks move as words");
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     constexpr int R = chunk_meta_slots(S);
-    constexpr int LD = chunk_loads_per_tile(LX4);
-    constexpr int ST = chunk_stores_per_tile(SX4);
-    constexpr uint32_t kData = kChunkDataSlotBytes;   // 4 KiB per data slot
+    constexpr int LD = chunk_loads_per_tile(LX4, W);
+    constexpr int ST = chunk_stores_per_tile(SX4, W);
+    constexpr int WPC = W / 4;                        // words per chunk
+    constexpr uint32_t kData = chunk_data_slot_bytes(W);   // 256 chunks per data slot
     constexpr uint32_t kMeta = kChunkMetaSlotBytes;   // 3 KiB per metadata slot
 
     const uint32_t tid = threadIdx.x;
@@ -58,13 +63,13 @@ __global__ void __launch_bounds__(256) chunk_copy_kernel(ChunkParams p)
     const bool has_size = p.flags & kHasSize;
     const bool has_ign = p.flags & kHasIgnore;
 
-    const uint32_t run_end = span * 16;           // first out-of-range byte of src/dst
-    const BufferRes rsrc = make_buffer_res(p.src + 16 * first, run_end);
-    const BufferRes rdst = make_buffer_res(p.dst + 16 * first, run_end);
+    const uint32_t run_end = span * W;            // first out-of-range byte of src/dst
+    const BufferRes rsrc = make_buffer_res(p.src + W * first, run_end);
+    const BufferRes rdst = make_buffer_res(p.dst + W * first, run_end);
     // An absent metadata array still gets its loads issued (so counts stay
     // fixed); they read the run's own source bytes, and those LDS bytes are
     // ignored.
-    const uint8_t *src_run = p.src + 16 * first;
+    const uint8_t *src_run = p.src + W * first;
     const BufferRes rpred = make_buffer_res(has_pred ? p.pred + first : src_run, span);
     const BufferRes rsize = make_buffer_res(has_size ? p.src_size + first : src_run, span);
     const BufferRes rign = make_buffer_res(has_ign ? p.ignore_src + first : src_run, span);
@@ -83,7 +88,7 @@ __global__ void __launch_bounds__(256) chunk_copy_kernel(ChunkParams p)
         dma_u8(rign, voff, uniform(m0 + 512));
     };
 
-    // Effective byte count of the lane's chunk (0..16) and whether it is stored.
+    // Effective byte count of the lane's chunk (0..W) and whether it is stored.
     struct Meta {
         uint32_t keep;
         bool store;
@@ -92,8 +97,8 @@ __global__ void __launch_bounds__(256) chunk_copy_kernel(ChunkParams p)
         const uint8_t *m = lds + meta_ring + mslot * kMeta + meta_wave + lane * 4;
         const bool pr = has_pred ? m[0] != 0 : true;
         const bool ig = has_ign ? m[512] != 0 : false;
-        uint32_t s = has_size ? m[256] : 16u;
-        s = s > 16u ? 16u : s;
+        uint32_t s = has_size ? m[256] : (uint32_t)W;
+        s = s > (uint32_t)W ? (uint32_t)W : s;
         return Meta{ig ? 0u : s, pr};
     };
 
@@ -104,8 +109,8 @@ __global__ void __launch_bounds__(256) chunk_copy_kernel(ChunkParams p)
             const bool needed = m.store && m.keep != 0;
             dma_b128(rsrc, needed ? j * kData + tid * 16 : run_end, uniform(slot + wave_first * 16));
         } else {
-            static_for<0, 4>([&](auto q) TP_INLINE {
-                const uint32_t w0 = wave_first * 4 + q * 64;   // first word of this load
+            static_for<0, WPC>([&](auto q) TP_INLINE {
+                const uint32_t w0 = wave_first * WPC + q * 64;   // first word of this load
                 dma_b32(rsrc, j * kData + (w0 + lane) * 4, uniform(slot + w0 * 4));
             });
         }
@@ -113,19 +118,26 @@ __global__ void __launch_bounds__(256) chunk_copy_kernel(ChunkParams p)
 
     auto consume = [&](uint32_t j, uint32_t dslot, uint32_t mslot) TP_INLINE {
         const Meta m = read_meta(mslot);
-        u32x4 v = *reinterpret_cast<const u32x4 *>(lds + data_ring + dslot * kData + tid * 16);
+        u32x4 v;
+        if constexpr (W == 16) {
+            v = *reinterpret_cast<const u32x4 *>(lds + data_ring + dslot * kData + tid * 16);
+        } else {
+            static_for<0, WPC>([&](auto w) TP_INLINE {
+                v[(int)w] = *reinterpret_cast<const uint32_t *>(lds + data_ring + dslot * kData + tid * W + w * 4);
+            });
+        }
         // keep bytes [0, keep): word w keeps min(max(keep - 4w, 0), 4) bytes
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < WPC; ++w) {
             const int kb = (int)m.keep - 4 * w;
             const uint32_t mask = kb >= 4 ? 0xFFFFFFFFu : kb <= 0 ? 0u : ((1u << (8 * kb)) - 1u);
             v[w] &= mask;
         }
-        const uint32_t off = j * kData + tid * 16;
+        const uint32_t off = j * kData + tid * W;
         if constexpr (SX4) {
             store_b128(rdst, m.store ? off : run_end, v);
         } else {
-            static_for<0, 4>([&](auto w) TP_INLINE { store_b32(rdst, m.store ? off + w * 4 : run_end, v[(int)w]); });
+            static_for<0, WPC>([&](auto w) TP_INLINE { store_b32(rdst, m.store ? off + w * 4 : run_end, v[(int)w]); });
         }
     };
 
@@ -180,14 +192,17 @@ __global__ void __launch_bounds__(256) chunk_copy_kernel(ChunkParams p)
 int launch_chunk_copy(const tp_plan &plan, const ChunkParams &p, void *stream)
 {
     using Fn = void (*)(ChunkParams);
-#define TP_CHUNK_ROW(S)                                                                    \
-    &dev::chunk_copy_kernel<S, true, true>, &dev::chunk_copy_kernel<S, false, true>,       \
-        &dev::chunk_copy_kernel<S, true, false>, &dev::chunk_copy_kernel<S, false, false>
-    static constexpr Fn table[kMaxStages * 4] = {TP_CHUNK_ROW(1), TP_CHUNK_ROW(2), TP_CHUNK_ROW(3),
+    // per stage count: the four 16-byte-chunk paths, then 8- and 4-byte chunks (words only)
+#define TP_CHUNK_ROW(S)                                                                        \
+    &dev::chunk_copy_kernel<S, 16, true, true>, &dev::chunk_copy_kernel<S, 16, false, true>,   \
+        &dev::chunk_copy_kernel<S, 16, true, false>, &dev::chunk_copy_kernel<S, 16, false, false>, \
+        &dev::chunk_copy_kernel<S, 8, false, false>, &dev::chunk_copy_kernel<S, 4, false, false>
+    static constexpr Fn table[kMaxStages * 6] = {TP_CHUNK_ROW(1), TP_CHUNK_ROW(2), TP_CHUNK_ROW(3),
                                                  TP_CHUNK_ROW(4), TP_CHUNK_ROW(5), TP_CHUNK_ROW(6),
                                                  TP_CHUNK_ROW(7), TP_CHUNK_ROW(8)};
 #undef TP_CHUNK_ROW
-    const Fn fn = table[(plan.stages - 1) * 4 + plan.path];
+    const int col = plan.chunk_bytes == 16 ? plan.path : plan.chunk_bytes == 8 ? 4 : 5;
+    const Fn fn = table[(plan.stages - 1) * 6 + col];
     if (plan.lds_bytes > 65536) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,

@@ -112,14 +112,17 @@ struct Map2dParams {
 };
 
 // ---------------------------------------------------------- chunk copy
-TP_HD constexpr int chunk_loads_per_tile(bool load_x4)
+// Memory instructions per lane and tile of the chunk copy, for chunks of
+// `width` = 4, 8 or 16 bytes: three metadata bytes, then the chunk as one
+// 16-byte load when that is aligned, else as width / 4 words.
+TP_HD constexpr int chunk_loads_per_tile(bool load_x4, int width = 16)
 {
-    return kChunkMetaArrays + (load_x4 ? 1 : 4);
+    return kChunkMetaArrays + (width == 16 && load_x4 ? 1 : width / 4);
 }
 
-TP_HD constexpr int chunk_stores_per_tile(bool store_x4)
+TP_HD constexpr int chunk_stores_per_tile(bool store_x4, int width = 16)
 {
-    return store_x4 ? 1 : 4;
+    return width == 16 && store_x4 ? 1 : width / 4;
 }
 
 TP_HD constexpr int chunk_meta_slots(int stages)
@@ -127,12 +130,13 @@ TP_HD constexpr int chunk_meta_slots(int stages)
     return stages == 1 ? 1 : 2 * stages - 1;
 }
 
-constexpr int kChunkDataSlotBytes = kChunkTile * 16;                    // 4 KiB
+TP_HD constexpr int chunk_data_slot_bytes(int width = 16) { return kChunkTile * width; }
+constexpr int kChunkDataSlotBytes = kChunkTile * 16;                    // 4 KiB (16-byte chunks)
 constexpr int kChunkMetaSlotBytes = kChunkMetaArrays * kChunkTile * 4;  // 3 KiB (4 bytes per lane)
 
-TP_HD constexpr int chunk_lds_bytes(int stages)
+TP_HD constexpr int chunk_lds_bytes(int stages, int width = 16)
 {
-    return stages * kChunkDataSlotBytes + chunk_meta_slots(stages) * kChunkMetaSlotBytes;
+    return stages * chunk_data_slot_bytes(width) + chunk_meta_slots(stages) * kChunkMetaSlotBytes;
 }
 
 enum ChunkFlags : int32_t {
@@ -175,9 +179,9 @@ void map2d_resolve_box(int64_t cols, int *box_rows, int *box_cols);
 int plan_map_2d(uintptr_t src, int64_t src_stride, uintptr_t dst, int64_t dst_stride,
                 int64_t rows, int64_t cols, int op, int box_rows, int box_cols, int stages,
                 int tiles_per_block, int64_t lds_budget, tp_plan *plan);
-int plan_chunk_copy(uintptr_t src, uintptr_t dst, int64_t n_chunks, uintptr_t pred,
-                    uintptr_t src_size, uintptr_t ignore_src, int stages, int tiles_per_block,
-                    int64_t lds_budget, tp_plan *plan);
+int plan_chunk_copy(uintptr_t src, uintptr_t dst, int64_t n_chunks, int chunk_bytes,
+                    uintptr_t pred, uintptr_t src_size, uintptr_t ignore_src, int stages,
+                    int tiles_per_block, int64_t lds_budget, tp_plan *plan);
 
 // Horner coefficients c_k = RN(1/(k+1)), k = 0..31.
 void horner32_coefficients(float c[32]);

@@ -270,18 +270,20 @@ int plan_map_2d(uintptr_t src, int64_t src_stride, uintptr_t dst, int64_t dst_st
     return TP_OK;
 }
 
-int plan_chunk_copy(uintptr_t src, uintptr_t dst, int64_t n_chunks, uintptr_t pred,
-                    uintptr_t src_size, uintptr_t ignore_src, int stages, int tiles_per_block,
-                    int64_t lds_budget, tp_plan *plan)
+int plan_chunk_copy(uintptr_t src, uintptr_t dst, int64_t n_chunks, int chunk_bytes,
+                    uintptr_t pred, uintptr_t src_size, uintptr_t ignore_src, int stages,
+                    int tiles_per_block, int64_t lds_budget, tp_plan *plan)
 {
     if (n_chunks < 0 || n_chunks > kMaxChunks)
+        return TP_ERR_INVALID_ARG;
+    if (chunk_bytes != 4 && chunk_bytes != 8 && chunk_bytes != 16)
         return TP_ERR_INVALID_ARG;
     if (stages < 1 || stages > kMaxStages)
         return TP_ERR_INVALID_ARG;
     const int tpb = resolve_tiles_per_block(tiles_per_block, kDefaultChunkTilesPerBlock);
     if (tpb < 0)
         return TP_ERR_INVALID_ARG;
-    if ((int64_t)tpb * kChunkDataSlotBytes > kMaxRunBytes)
+    if ((int64_t)tpb * chunk_data_slot_bytes(chunk_bytes) > kMaxRunBytes)
         return TP_ERR_INVALID_ARG;
     tp_plan p;
     memset(&p, 0, sizeof p);
@@ -290,14 +292,15 @@ int plan_chunk_copy(uintptr_t src, uintptr_t dst, int64_t n_chunks, uintptr_t pr
     p.threads = kChunkTile;
     p.lane_chunks = 1;
     p.tiles_per_block = tpb;
-    p.lds_bytes = chunk_lds_bytes(stages);
+    p.chunk_bytes = chunk_bytes;
+    p.lds_bytes = chunk_lds_bytes(stages, chunk_bytes);
     p.ring_bytes = p.lds_bytes;
     if (n_chunks > 0) {
         if (!src || !dst)
             return TP_ERR_INVALID_ARG;
         if (src % 4 || dst % 4)
             return TP_ERR_MISALIGNED;
-        const uint64_t bytes = (uint64_t)n_chunks * 16;
+        const uint64_t bytes = (uint64_t)n_chunks * chunk_bytes;
         if (src != dst && overlaps(src, bytes, dst, bytes))
             return TP_ERR_OVERLAP;
         const uintptr_t meta[3] = {pred, src_size, ignore_src};
@@ -307,11 +310,16 @@ int plan_chunk_copy(uintptr_t src, uintptr_t dst, int64_t n_chunks, uintptr_t pr
     }
     if (p.lds_bytes > lds_budget)
         return TP_ERR_LDS_BUDGET;
-    p.path = n_chunks > 0 ? path_bits(src, dst) : TP_PATH_X4;
+    // 16-byte chunks move as one 16-byte access per side when that side is
+    // aligned; narrower chunks always move as words
+    if (chunk_bytes == 16)
+        p.path = n_chunks > 0 ? path_bits(src, dst) : TP_PATH_X4;
+    else
+        p.path = TP_PATH_SCALAR;
     const bool load_x4 = !(p.path & TP_PATH_SCALAR_LOAD);
     const bool store_x4 = !(p.path & TP_PATH_SCALAR_STORE);
-    p.wait_steady = stage_wait_count(stages, chunk_loads_per_tile(load_x4),
-                                     chunk_stores_per_tile(store_x4), stages);
+    p.wait_steady = stage_wait_count(stages, chunk_loads_per_tile(load_x4, chunk_bytes),
+                                     chunk_stores_per_tile(store_x4, chunk_bytes), stages);
     p.num_tiles = ceil_div(n_chunks, kChunkTile);
     p.grid = ceil_div(p.num_tiles, tpb);
     if (plan)

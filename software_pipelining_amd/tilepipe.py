@@ -61,7 +61,7 @@ class _CPlan(ctypes.Structure):
                 ("lds_bytes", ctypes.c_int32), ("wait_steady", ctypes.c_int32),
                 ("num_tiles", ctypes.c_int64), ("grid", ctypes.c_int64),
                 ("ring_bytes", ctypes.c_int32), ("resident_cap", ctypes.c_int32),
-                ("schedule", ctypes.c_int32)]
+                ("schedule", ctypes.c_int32), ("chunk_bytes", ctypes.c_int32)]
 
 
 @dataclass(frozen=True)
@@ -79,6 +79,7 @@ class Plan:
     ring_bytes: int
     resident_cap: int
     schedule: "Schedule"
+    chunk_bytes: int
 
 
 _lib = None
@@ -110,9 +111,10 @@ def _load():
         "tp_pipelined_map": ([vp, vp, i64, i32, i32, i32, i32, vp, ip], i32),
         "tp_pipelined_map_ex": ([vp, vp, i64, i32, i32, i32, i32, i32, i32, vp, ip], i32),
         "tp_chunk_copy": ([vp, vp, i64, vp, vp, vp, i32, i32, vp, ip], i32),
+        "tp_chunk_copy_ex": ([vp, vp, i64, i32, vp, vp, vp, i32, i32, vp, ip], i32),
         "tp_plan_row_shift": ([vp, vp, i64, i64, pp], i32),
         "tp_plan_pipelined_map": ([vp, vp, i64, i32, i32, i32, i32, i32, i32, i64, pp], i32),
-        "tp_plan_chunk_copy": ([vp, vp, i64, vp, vp, vp, i32, i32, i64, pp], i32),
+        "tp_plan_chunk_copy": ([vp, vp, i64, i32, vp, vp, vp, i32, i32, i64, pp], i32),
         "tp_map_2d": ([vp, i64, vp, i64, i64, i64, i32, i32, i32, i32, i32, vp, ip], i32),
         "tp_plan_map_2d": ([vp, i64, vp, i64, i64, i64, i32, i32, i32, i32, i32, i64, pp], i32),
     }
@@ -254,15 +256,18 @@ def map_2d(src, dst, op: str = "scale2", box_rows: int = 0, box_cols: int = 0,
 
 
 def chunk_copy(src, dst, pred=None, src_size=None, ignore_src=None, stages: int = 2,
-               tiles_per_block: int = 0, stream=None) -> Path:
-    """Predicated copy of 16-byte chunks: src/dst are uint8 GPU tensors of
-    n_chunks*16 bytes; pred/src_size/ignore_src uint8 tensors of n_chunks (or None)."""
+               tiles_per_block: int = 0, stream=None, chunk_bytes: int = 16) -> Path:
+    """Predicated copy of chunks of chunk_bytes (4, 8 or 16) bytes: src/dst are
+    uint8 GPU tensors of n_chunks*chunk_bytes bytes; pred/src_size/ignore_src
+    uint8 tensors of n_chunks (or None)."""
     import torch
     _require(src, torch.uint8, "src")
     _require(dst, torch.uint8, "dst")
-    if src.numel() != dst.numel() or src.numel() % 16:
-        raise ValueError("src and dst must hold the same whole number of 16-byte chunks")
-    n = src.numel() // 16
+    if chunk_bytes not in (4, 8, 16):
+        raise ValueError("chunk_bytes must be 4, 8 or 16")
+    if src.numel() != dst.numel() or src.numel() % chunk_bytes:
+        raise ValueError(f"src and dst must hold the same whole number of {chunk_bytes}-byte chunks")
+    n = src.numel() // chunk_bytes
     ptrs = []
     for name, m in (("pred", pred), ("src_size", src_size), ("ignore_src", ignore_src)):
         if m is None:
@@ -275,10 +280,11 @@ def chunk_copy(src, dst, pred=None, src_size=None, ignore_src=None, stages: int 
     _same_device(src, dst, pred, src_size, ignore_src)
     path = ctypes.c_int(0)
     with torch.cuda.device(src.device):
-        st = _load().tp_chunk_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
-                                   n, *ptrs, stages, tiles_per_block, _stream_handle(src, stream),
-                                   ctypes.byref(path))
-    _check(st, "tp_chunk_copy")
+        st = _load().tp_chunk_copy_ex(ctypes.c_void_p(src.data_ptr()),
+                                      ctypes.c_void_p(dst.data_ptr()), n, chunk_bytes, *ptrs,
+                                      stages, tiles_per_block, _stream_handle(src, stream),
+                                      ctypes.byref(path))
+    _check(st, "tp_chunk_copy_ex")
     return Path(path.value)
 
 
@@ -290,7 +296,7 @@ def _plan(status: int, cp: _CPlan, where: str) -> Plan:
     _check(status, where)
     return Plan(Path(cp.path), cp.stages, cp.tile_units, cp.threads, cp.lane_chunks,
                 cp.tiles_per_block, cp.lds_bytes, cp.wait_steady, cp.num_tiles, cp.grid,
-                cp.ring_bytes, cp.resident_cap, Schedule(cp.schedule))
+                cp.ring_bytes, cp.resident_cap, Schedule(cp.schedule), cp.chunk_bytes)
 
 
 def plan_row_shift(a_ptr: int, b_ptr: int, rows: int, lds_budget: int = _NO_BUDGET) -> Plan:
@@ -324,10 +330,11 @@ def plan_map_2d(src_ptr: int, src_stride: int, dst_ptr: int, dst_stride: int, ro
 
 def plan_chunk_copy(src_ptr: int, dst_ptr: int, n_chunks: int, pred_ptr: int = 0,
                     size_ptr: int = 0, ignore_ptr: int = 0, stages: int = 2,
-                    tiles_per_block: int = 0, lds_budget: int = _NO_BUDGET) -> Plan:
+                    tiles_per_block: int = 0, lds_budget: int = _NO_BUDGET,
+                    chunk_bytes: int = 16) -> Plan:
     cp = _CPlan()
     st = _load().tp_plan_chunk_copy(ctypes.c_void_p(src_ptr), ctypes.c_void_p(dst_ptr), n_chunks,
-                                    ctypes.c_void_p(pred_ptr or None),
+                                    chunk_bytes, ctypes.c_void_p(pred_ptr or None),
                                     ctypes.c_void_p(size_ptr or None),
                                     ctypes.c_void_p(ignore_ptr or None), stages, tiles_per_block,
                                     lds_budget, ctypes.byref(cp))

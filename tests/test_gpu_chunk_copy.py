@@ -132,3 +132,31 @@ def test_chunk_copy_errors(cuda_device):
     with pytest.raises(tp.TilepipeError) as e:
         tp.chunk_copy(src, dst[:64 * 16], stages=0)
     assert e.value.status == 1
+
+
+@pytest.mark.parametrize("width", [4, 8])
+def test_narrow_chunks(cuda_device, width):
+    # 4- and 8-byte chunks: every operand combination, absent arrays, stages, runs
+    rng = np.random.default_rng(width)
+    for n in (1, 255, 256, 1000, 5 * 256 + 77):
+        src_h = rng.integers(0, 256, size=n * width, dtype=np.uint8)
+        dst_h = np.frombuffer(np.full(-(-n * width // 4), DEADBEEF, np.uint32).tobytes(),
+                              np.uint8)[:n * width].copy()
+        pred_h = rng.integers(0, 3, size=n).astype(np.uint8)          # 0 false, 1-2 true
+        size_h = rng.integers(0, width + 3, size=n).astype(np.uint8)  # past width: clamped
+        ign_h = (rng.random(n) < 0.05).astype(np.uint8)
+        for stages in (1, 2, 4):
+            for tpb in (0, 1, 3):
+                for use in ((True, True, True), (False, True, False), (False, False, False)):
+                    metas = [m if u else None for m, u in zip((pred_h, size_h, ign_h), use)]
+                    src = to_device(torch.from_numpy(src_h), cuda_device)
+                    dst = Guarded(n * width, torch.uint8, cuda_device, fill_word=DEADBEEF)
+                    devm = [_meta(None if m is None else torch.from_numpy(m), cuda_device)
+                            for m in metas]
+                    path = tp.chunk_copy(src.tensor, dst.tensor, *(d[1] for d in devm),
+                                         stages=stages, tiles_per_block=tpb, chunk_bytes=width)
+                    assert path == tp.Path.SCALAR
+                    expected = oracle.chunk_copy(src_h, dst_h, *metas, chunk_bytes=width)
+                    what = f"W={width} n={n} S={stages} T={tpb} use={use}"
+                    assert_bits_equal(dst.tensor, expected, what)
+                    assert dst.guards_intact() and src.guards_intact(), what

@@ -40,9 +40,9 @@ def test_status_strings():
     assert lib.tp_status_string(99).decode() == "TP_ERR_UNKNOWN"
 
 
-def _status(fn, *args):
+def _status(fn, *args, **kwargs):
     try:
-        fn(*args)
+        fn(*args, **kwargs)
         return 0
     except tp.TilepipeError as e:
         return e.status
@@ -380,6 +380,24 @@ def test_chunk_copy_plan_errors():
     assert tp.plan_chunk_copy(A, B, 100, B + 1600, A, A).grid == 1   # metadata may alias src
     assert _status(tp.plan_chunk_copy, A, B, 1, 0, 0, 0, 9) == 1
     assert _status(tp.plan_chunk_copy, A, B, 1, 0, 0, 0, 8, 0, 8 * 4096) == 3
+
+
+def test_chunk_copy_widths_plan():
+    # 4- and 8-byte chunks move as words on both sides; the ring holds 256 chunks per slot
+    for w, ld, st in ((4, 1, 1), (8, 2, 2), (16, 1, 1)):
+        p = tp.plan_chunk_copy(A, B, 1000, stages=3, chunk_bytes=w)
+        assert p.chunk_bytes == w and p.threads == 256
+        assert p.path == (tp.Path.X4 if w == 16 else tp.Path.SCALAR)
+        assert p.ring_bytes == 3 * 256 * w + 5 * 3 * 256 * 4
+        assert p.wait_steady == 1 * (3 + ld) + 2 * st                      # (S-2) ld + (S-1) st
+        assert (p.num_tiles, p.grid) == (4, 1)
+    assert tp.plan_chunk_copy(A + 4, B + 4, 10, chunk_bytes=8).path == tp.Path.SCALAR
+    assert tp.plan_chunk_copy(A, B, 10).chunk_bytes == 16
+    for bad in (0, 2, 12, 32):
+        assert _status(tp.plan_chunk_copy, A, B, 10, chunk_bytes=bad) == 1
+    # overlap is judged on n x chunk_bytes bytes
+    assert tp.plan_chunk_copy(A, A + 400, 100, chunk_bytes=4).grid == 1
+    assert _status(tp.plan_chunk_copy, A, A + 400, 101, chunk_bytes=4) == 4
 
 
 def test_binding_rejects_cpu_tensors():
