@@ -179,6 +179,8 @@ int plan_map(uintptr_t in, uintptr_t out, int64_t n, int op, int tile_elems, int
     const int64_t n_main = n & ~int64_t(3);
     p.num_tiles = ceil_div(n_main, tile_elems);
     p.grid = n == 0 ? 0 : (p.num_tiles == 0 ? 1 : ceil_div(p.num_tiles, tpb));
+    if (p.grid > INT32_MAX)        // more workgroups than one launch can name
+        return TP_ERR_INVALID_ARG;
     if (plan)
         *plan = p;
     return TP_OK;
@@ -322,6 +324,8 @@ int plan_chunk_copy(uintptr_t src, uintptr_t dst, int64_t n_chunks, int chunk_by
                                      chunk_stores_per_tile(store_x4, chunk_bytes), stages);
     p.num_tiles = ceil_div(n_chunks, kChunkTile);
     p.grid = ceil_div(p.num_tiles, tpb);
+    if (p.grid > INT32_MAX)
+        return TP_ERR_INVALID_ARG;
     if (plan)
         *plan = p;
     return TP_OK;

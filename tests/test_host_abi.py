@@ -128,6 +128,11 @@ def test_map_plan_option_errors():
     assert _status(tp.plan_map, A, B, 10, "scale2", 8192, 2, 65536) == 1   # run > 1 GiB
     assert _status(tp.plan_map, A, B, 10, "scale2", 1024, 2, -3) == 1
     assert _status(tp.plan_map, A, B, 1 << 41) == 1
+    # 2^40 floats in 256-float tiles, runs of one: 2^32 workgroups, more than a launch names
+    far_a, far_b = 1 << 44, 1 << 45                                        # 4 TiB buffers
+    assert _status(tp.plan_map, far_a, far_b, 1 << 40, "scale2", 256, 1, 1) == 1
+    assert _status(tp.plan_map, far_a, far_b, 1 << 40, "scale2", 256, 1, 2) == 1   # 2^31 WGs
+    assert tp.plan_map(far_a, far_b, 1 << 40, "scale2", 256, 1, 4).grid == 1 << 30
     # exact aliasing is allowed; n == 0 accepts null pointers
     assert tp.plan_map(A, A, 10).grid == 1
     assert tp.plan_map(0, 0, 0).grid == 0
