@@ -544,8 +544,23 @@ def extra_rows(args, tp, workloads, torch, np, dev, x_host, xbuf, y):
     a = workloads.arange_rows(64).to(dev)
     b = torch.empty_like(a)
     per, region = time_launches(lambda: tp.row_shift(a, b), 10, 1000)
+    # the same 1000 launches captured once in a HIP graph and replayed: the
+    # time per kernel without the host's per-call work
+    g = torch.cuda.CUDAGraph()
+    tp.row_shift(a, b)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for _ in range(1000):
+            tp.row_shift(a, b)
+    g.replay()
+    torch.cuda.synchronize()
+    graph_ms = time_region(g.replay, 2, 5) / 5
     rows["row_shift"] = {"rows": 64, "median_launch_us": round(median(per) * 1e3, 2),
-                         "region_us_per_call": round(region, 4)}
+                         "region_us_per_call": round(region, 4),
+                         "graph_replay_us_per_kernel": round(graph_ms, 4)}
+    ok = np.array_equal(b.cpu().numpy().view(np.uint32),
+                        __import__("oracle").row_shift(a.cpu().numpy()).view(np.uint32))
+    rows["row_shift"]["parity"] = bool(ok)
     return rows
 
 
