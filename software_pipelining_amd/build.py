@@ -36,10 +36,18 @@ HIP_FLAGS = [
 ]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall", "-Wextra", "-Werror"]
 
-HIP_SOURCES = ["tp_row_shift.hip", "tp_chunk_copy.hip", "tp_map_scale2.hip",
-               "tp_map_horner32.hip", "tp_map_copy.hip", "tp_map_split_scale2.hip",
-               "tp_map_split_horner32.hip", "tp_map_split_copy.hip", "tp_map2d_scale2.hip",
-               "tp_map2d_horner32.hip", "tp_map2d_copy.hip", "tp_api.cpp"]
+# The kernel families are instantiated per op and per half of the stage range
+# (one compilation of tp_<family>_inst.hip each), heaviest first, so the
+# pieces spread evenly over the compile jobs.
+_OPS = (("scale2", "TP_OP_SCALE2"), ("horner32", "TP_OP_HORNER32"), ("copy", "TP_OP_COPY"))
+_HALVES = ((1, 4), (5, 8))
+INSTANCES = [
+    (f"tp_{fam}_inst.hip", f"tp_{fam}_{op}_s{lo}_{hi}",
+     [f"-DTP_INST_OP={macro}", f"-DTP_INST_SLO={lo}", f"-DTP_INST_SHI={hi}",
+      f"-DTP_INST_FN=launch_{fam}_{op}_s{lo}_{hi}"])
+    for fam in ("map2d", "map_split", "map") for lo, hi in reversed(_HALVES) for op, macro in _OPS
+]
+HIP_SOURCES = ["tp_chunk_copy.hip", "tp_row_shift.hip", "tp_api.cpp"]
 CXX_SOURCES = ["tp_plan.cpp"]
 
 
@@ -53,15 +61,18 @@ def _run(cmd):
     return "\n".join(lines)
 
 
-def _compile(src: str, save_temps: bool = False) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(unit, save_temps: bool = False) -> str:
+    """unit: a source file name, or (source, object stem, extra flags)."""
+    src, stem, defs = (unit, os.path.splitext(unit)[0], []) if isinstance(unit, str) else unit
+    obj = os.path.join(BUILD, stem + ".o")
     path = os.path.join(CSRC, src)
     if src in CXX_SOURCES:
         cmd = ["g++", *CXX_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c", path, "-o", obj]
     else:
-        cmd = [HIPCC, *HIP_FLAGS, "-x", "hip", f"-I{INCLUDE}", f"-I{CSRC}", "-c", path, "-o", obj]
+        cmd = [HIPCC, *HIP_FLAGS, *defs, "-x", "hip", f"-I{INCLUDE}", f"-I{CSRC}", "-c", path,
+               "-o", obj]
         if save_temps:
-            cmd += ["--save-temps"]
+            cmd += ["-save-temps=obj"]
     _run(cmd)
     return obj
 
@@ -70,16 +81,10 @@ def build(jobs: int | None = None, verbose: bool = True, save_temps: bool = Fals
     """Compile every translation unit and link libtilepipe.so; return its path."""
     os.makedirs(BUILD, exist_ok=True)
     t0 = time.time()
-    srcs = HIP_SOURCES + CXX_SOURCES
-    jobs = jobs or min(len(srcs), max(1, os.cpu_count() or 1))
-    cwd = os.getcwd()
-    if save_temps:
-        os.chdir(BUILD)
-    try:
-        with ThreadPoolExecutor(max_workers=jobs) as ex:
-            objs = list(ex.map(lambda s: _compile(s, save_temps), srcs))
-    finally:
-        os.chdir(cwd)
+    units = INSTANCES + HIP_SOURCES + CXX_SOURCES
+    jobs = jobs or min(len(units), max(1, os.cpu_count() or 1))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda u: _compile(u, save_temps), units))
     tmp = LIB + ".tmp%d" % os.getpid()
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)

@@ -81,6 +81,49 @@ int finish_launch(int hip_error)
     return TP_OK;
 }
 
+// The kernel instances of each family, op and half of the stage range live in
+// separate objects; these pick the one a plan needs.
+int launch_map(const tp_plan &plan, const tp::MapParams &p, int op, void *stream)
+{
+    const bool hi = plan.stages > 4;
+    if (plan.schedule == TP_SCHED_ROLE_SPLIT) {
+        switch (op) {
+        case TP_OP_SCALE2:
+            return hi ? tp::launch_map_split_scale2_s5_8(plan, p, stream)
+                      : tp::launch_map_split_scale2_s1_4(plan, p, stream);
+        case TP_OP_HORNER32:
+            return hi ? tp::launch_map_split_horner32_s5_8(plan, p, stream)
+                      : tp::launch_map_split_horner32_s1_4(plan, p, stream);
+        default:
+            return hi ? tp::launch_map_split_copy_s5_8(plan, p, stream)
+                      : tp::launch_map_split_copy_s1_4(plan, p, stream);
+        }
+    }
+    switch (op) {
+    case TP_OP_SCALE2:
+        return hi ? tp::launch_map_scale2_s5_8(plan, p, stream) : tp::launch_map_scale2_s1_4(plan, p, stream);
+    case TP_OP_HORNER32:
+        return hi ? tp::launch_map_horner32_s5_8(plan, p, stream)
+                  : tp::launch_map_horner32_s1_4(plan, p, stream);
+    default:
+        return hi ? tp::launch_map_copy_s5_8(plan, p, stream) : tp::launch_map_copy_s1_4(plan, p, stream);
+    }
+}
+
+int launch_map2d(const tp_plan &plan, const tp::Map2dParams &p, int op, void *stream)
+{
+    const bool hi = plan.stages > 4;
+    switch (op) {
+    case TP_OP_SCALE2:
+        return hi ? tp::launch_map2d_scale2_s5_8(plan, p, stream) : tp::launch_map2d_scale2_s1_4(plan, p, stream);
+    case TP_OP_HORNER32:
+        return hi ? tp::launch_map2d_horner32_s5_8(plan, p, stream)
+                  : tp::launch_map2d_horner32_s1_4(plan, p, stream);
+    default:
+        return hi ? tp::launch_map2d_copy_s5_8(plan, p, stream) : tp::launch_map2d_copy_s1_4(plan, p, stream);
+    }
+}
+
 // Argument errors are decided with an unlimited LDS budget first, so a bad
 // call never touches the device; the device's real budget is checked after.
 constexpr int64_t kNoBudget = INT64_MAX;
@@ -207,21 +250,7 @@ TP_API int tp_pipelined_map_ex(const float *in, float *out, int64_t n, int op, i
     p.n_main = n & ~int64_t(3);
     p.tiles_per_block = plan.tiles_per_block;
     tp::horner32_coefficients(p.coef);
-    int e = 0;
-    if (plan.schedule == TP_SCHED_ROLE_SPLIT) {
-        switch (op) {
-        case TP_OP_SCALE2: e = tp::launch_map_split_scale2(plan, p, stream); break;
-        case TP_OP_HORNER32: e = tp::launch_map_split_horner32(plan, p, stream); break;
-        default: e = tp::launch_map_split_copy(plan, p, stream); break;
-        }
-    } else {
-        switch (op) {
-        case TP_OP_SCALE2: e = tp::launch_map_scale2(plan, p, stream); break;
-        case TP_OP_HORNER32: e = tp::launch_map_horner32(plan, p, stream); break;
-        default: e = tp::launch_map_copy(plan, p, stream); break;
-        }
-    }
-    return finish_launch(e);
+    return finish_launch(launch_map(plan, p, op, stream));
 }
 
 TP_API int tp_map_2d(const float *src, int64_t src_stride, float *dst, int64_t dst_stride,
@@ -261,13 +290,7 @@ TP_API int tp_map_2d(const float *src, int64_t src_stride, float *dst, int64_t d
     p.runs_per_band = (int32_t)((((cols + box_cols - 1) / box_cols) + plan.tiles_per_block - 1) /
                                 plan.tiles_per_block);
     tp::horner32_coefficients(p.coef);
-    int e = 0;
-    switch (op) {
-    case TP_OP_SCALE2: e = tp::launch_map2d_scale2(plan, p, stream); break;
-    case TP_OP_HORNER32: e = tp::launch_map2d_horner32(plan, p, stream); break;
-    default: e = tp::launch_map2d_copy(plan, p, stream); break;
-    }
-    return finish_launch(e);
+    return finish_launch(launch_map2d(plan, p, op, stream));
 }
 
 TP_API int tp_chunk_copy(const void *src, void *dst, int64_t n_chunks, const uint8_t *pred,

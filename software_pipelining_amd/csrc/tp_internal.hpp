@@ -189,15 +189,26 @@ void horner32_coefficients(float c[32]);
 // ------------------------------------------------------- kernel launchers
 // Each returns a hipError_t value (0 = success). `stream` is a hipStream_t.
 int launch_row_shift(const tp_plan &plan, const RowShiftParams &p, void *stream);
-int launch_map_scale2(const tp_plan &plan, const MapParams &p, void *stream);
-int launch_map_horner32(const tp_plan &plan, const MapParams &p, void *stream);
-int launch_map_copy(const tp_plan &plan, const MapParams &p, void *stream);
-int launch_map_split_scale2(const tp_plan &plan, const MapParams &p, void *stream);
-int launch_map_split_horner32(const tp_plan &plan, const MapParams &p, void *stream);
-int launch_map_split_copy(const tp_plan &plan, const MapParams &p, void *stream);
-int launch_map2d_scale2(const tp_plan &plan, const Map2dParams &p, void *stream);
-int launch_map2d_horner32(const tp_plan &plan, const Map2dParams &p, void *stream);
-int launch_map2d_copy(const tp_plan &plan, const Map2dParams &p, void *stream);
+// One entry per kernel family, op and half of the stage range (S 1-4, 5-8),
+// each defined by its own compilation of tp_*_inst.hip.
+int launch_map_scale2_s1_4(const tp_plan &plan, const MapParams &p, void *stream);
+int launch_map_scale2_s5_8(const tp_plan &plan, const MapParams &p, void *stream);
+int launch_map_horner32_s1_4(const tp_plan &plan, const MapParams &p, void *stream);
+int launch_map_horner32_s5_8(const tp_plan &plan, const MapParams &p, void *stream);
+int launch_map_copy_s1_4(const tp_plan &plan, const MapParams &p, void *stream);
+int launch_map_copy_s5_8(const tp_plan &plan, const MapParams &p, void *stream);
+int launch_map_split_scale2_s1_4(const tp_plan &plan, const MapParams &p, void *stream);
+int launch_map_split_scale2_s5_8(const tp_plan &plan, const MapParams &p, void *stream);
+int launch_map_split_horner32_s1_4(const tp_plan &plan, const MapParams &p, void *stream);
+int launch_map_split_horner32_s5_8(const tp_plan &plan, const MapParams &p, void *stream);
+int launch_map_split_copy_s1_4(const tp_plan &plan, const MapParams &p, void *stream);
+int launch_map_split_copy_s5_8(const tp_plan &plan, const MapParams &p, void *stream);
+int launch_map2d_scale2_s1_4(const tp_plan &plan, const Map2dParams &p, void *stream);
+int launch_map2d_scale2_s5_8(const tp_plan &plan, const Map2dParams &p, void *stream);
+int launch_map2d_horner32_s1_4(const tp_plan &plan, const Map2dParams &p, void *stream);
+int launch_map2d_horner32_s5_8(const tp_plan &plan, const Map2dParams &p, void *stream);
+int launch_map2d_copy_s1_4(const tp_plan &plan, const Map2dParams &p, void *stream);
+int launch_map2d_copy_s5_8(const tp_plan &plan, const Map2dParams &p, void *stream);
 int launch_chunk_copy(const tp_plan &plan, const ChunkParams &p, void *stream);
 
 }  // namespace tp

@@ -157,35 +157,34 @@ __global__ void __launch_bounds__(256) map_kernel(MapParams p)
     // before it returns, and the tail waits for its own.
 }
 
-// Kernel table of one op: index ((S-1) * 4 + log2 L) * 4 + path.
+// Kernel table of one op over stage counts SLO..SHI:
+// index ((S - SLO) * 4 + log2 L) * 4 + path.
 using MapKernelFn = void (*)(MapParams);
 
-template <int OP, int I>
+template <int OP, int SLO, int I>
 constexpr MapKernelFn map_entry()
 {
     constexpr int path = I % 4;
     constexpr int L = 1 << ((I / 4) % 4);
-    constexpr int S = I / 16 + 1;
+    constexpr int S = SLO + I / 16;
     return &map_kernel<OP, S, L, !(path & TP_PATH_SCALAR_LOAD), !(path & TP_PATH_SCALAR_STORE)>;
 }
 
-template <int OP, int... I>
+template <int OP, int SLO, int... I>
 constexpr std::array<MapKernelFn, sizeof...(I)> map_table(std::integer_sequence<int, I...>)
 {
-    return {map_entry<OP, I>()...};
+    return {map_entry<OP, SLO, I>()...};
 }
 
-constexpr int map_table_index(int stages, int lane_chunks, int path)
+constexpr int lane_chunks_index(int lane_chunks)
 {
-    const int li = lane_chunks == 1 ? 0 : lane_chunks == 2 ? 1 : lane_chunks == 4 ? 2 : 3;
-    return ((stages - 1) * 4 + li) * 4 + path;
+    return lane_chunks == 1 ? 0 : lane_chunks == 2 ? 1 : lane_chunks == 4 ? 2 : 3;
 }
 
-template <int OP>
-int launch_map_op(const tp_plan &plan, const MapParams &p, void *stream)
+// Launch a kernel of `fn`'s signature with the plan's grid, block and LDS.
+template <class Fn, class Params>
+int launch_planned(Fn fn, const tp_plan &plan, const Params &p, void *stream)
 {
-    static constexpr auto table = map_table<OP>(std::make_integer_sequence<int, kMaxStages * 4 * 4>{});
-    const MapKernelFn fn = table[map_table_index(plan.stages, plan.lane_chunks, plan.path)];
     if (plan.lds_bytes > 65536) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -193,11 +192,19 @@ int launch_map_op(const tp_plan &plan, const MapParams &p, void *stream)
         if (e != hipSuccess)
             return (int)e;
     }
-    MapParams args = p;
+    Params args = p;
     void *kargs[] = {&args};
     return (int)hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3((uint32_t)plan.grid),
                                 dim3((uint32_t)plan.threads), kargs, (size_t)plan.lds_bytes,
                                 (hipStream_t)stream);
+}
+
+template <int OP, int SLO, int SHI>
+int launch_map_stages(const tp_plan &plan, const MapParams &p, void *stream)
+{
+    static constexpr auto table = map_table<OP, SLO>(std::make_integer_sequence<int, (SHI - SLO + 1) * 16>{});
+    const int i = ((plan.stages - SLO) * 4 + lane_chunks_index(plan.lane_chunks)) * 4 + plan.path;
+    return launch_planned(table[i], plan, p, stream);
 }
 
 }  // namespace dev

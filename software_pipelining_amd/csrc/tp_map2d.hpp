@@ -115,41 +115,31 @@ __global__ void __launch_bounds__(256) map2d_kernel(Map2dParams p)
     pipeline_run<S, LD, ST, map_wave_local(LX4, SX4)>(cnt, ring, tile_bytes, issue, consume);
 }
 
-// Kernel table of one op: index ((S-1) * 4 + log2 L) * 4 + path.
+// Kernel table of one op over stage counts SLO..SHI:
+// index ((S - SLO) * 4 + log2 L) * 4 + path.
 using Map2dKernelFn = void (*)(Map2dParams);
 
-template <int OP, int I>
+template <int OP, int SLO, int I>
 constexpr Map2dKernelFn map2d_entry()
 {
     constexpr int path = I % 4;
     constexpr int L = 1 << ((I / 4) % 4);
-    constexpr int S = I / 16 + 1;
+    constexpr int S = SLO + I / 16;
     return &map2d_kernel<OP, S, L, !(path & TP_PATH_SCALAR_LOAD), !(path & TP_PATH_SCALAR_STORE)>;
 }
 
-template <int OP, int... I>
+template <int OP, int SLO, int... I>
 constexpr std::array<Map2dKernelFn, sizeof...(I)> map2d_table(std::integer_sequence<int, I...>)
 {
-    return {map2d_entry<OP, I>()...};
+    return {map2d_entry<OP, SLO, I>()...};
 }
 
-template <int OP>
-int launch_map2d_op(const tp_plan &plan, const Map2dParams &p, void *stream)
+template <int OP, int SLO, int SHI>
+int launch_map2d_stages(const tp_plan &plan, const Map2dParams &p, void *stream)
 {
-    static constexpr auto table = map2d_table<OP>(std::make_integer_sequence<int, kMaxStages * 4 * 4>{});
-    const Map2dKernelFn fn = table[map_table_index(plan.stages, plan.lane_chunks, plan.path)];
-    if (plan.lds_bytes > 65536) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 plan.lds_bytes);
-        if (e != hipSuccess)
-            return (int)e;
-    }
-    Map2dParams args = p;
-    void *kargs[] = {&args};
-    return (int)hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3((uint32_t)plan.grid),
-                                dim3((uint32_t)plan.threads), kargs, (size_t)plan.lds_bytes,
-                                (hipStream_t)stream);
+    static constexpr auto table = map2d_table<OP, SLO>(std::make_integer_sequence<int, (SHI - SLO + 1) * 16>{});
+    const int i = ((plan.stages - SLO) * 4 + lane_chunks_index(plan.lane_chunks)) * 4 + plan.path;
+    return launch_planned(table[i], plan, p, stream);
 }
 
 }  // namespace dev

@@ -161,43 +161,32 @@ __global__ void __launch_bounds__(320) map_split_kernel(MapParams p)
     }
 }
 
-// Kernel table of one op: index ((S-1) * 6 + log2(tile / 256)) * 4 + path.
-template <int OP, int I>
+// Kernel table of one op over stage counts SLO..SHI:
+// index ((S - SLO) * 6 + log2(tile / 256)) * 4 + path.
+template <int OP, int SLO, int I>
 constexpr MapKernelFn map_split_entry()
 {
     constexpr int path = I % 4;
     constexpr int TILE = 256 << ((I / 4) % 6);
-    constexpr int S = I / 24 + 1;
+    constexpr int S = SLO + I / 24;
     return &map_split_kernel<OP, S, TILE, !(path & TP_PATH_SCALAR_LOAD), !(path & TP_PATH_SCALAR_STORE)>;
 }
 
-template <int OP, int... I>
+template <int OP, int SLO, int... I>
 constexpr std::array<MapKernelFn, sizeof...(I)> map_split_table(std::integer_sequence<int, I...>)
 {
-    return {map_split_entry<OP, I>()...};
+    return {map_split_entry<OP, SLO, I>()...};
 }
 
-template <int OP>
-int launch_map_split_op(const tp_plan &plan, const MapParams &p, void *stream)
+template <int OP, int SLO, int SHI>
+int launch_map_split_stages(const tp_plan &plan, const MapParams &p, void *stream)
 {
     static constexpr auto table =
-        map_split_table<OP>(std::make_integer_sequence<int, kMaxStages * 6 * 4>{});
+        map_split_table<OP, SLO>(std::make_integer_sequence<int, (SHI - SLO + 1) * 6 * 4>{});
     int ti = 0;
     while ((256 << ti) < plan.tile_units)
         ++ti;
-    const MapKernelFn fn = table[((plan.stages - 1) * 6 + ti) * 4 + plan.path];
-    if (plan.lds_bytes > 65536) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 plan.lds_bytes);
-        if (e != hipSuccess)
-            return (int)e;
-    }
-    MapParams args = p;
-    void *kargs[] = {&args};
-    return (int)hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3((uint32_t)plan.grid),
-                                dim3((uint32_t)plan.threads), kargs, (size_t)plan.lds_bytes,
-                                (hipStream_t)stream);
+    return launch_planned(table[((plan.stages - SLO) * 6 + ti) * 4 + plan.path], plan, p, stream);
 }
 
 }  // namespace dev
