@@ -120,13 +120,19 @@ def median(v):
     return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
 
 
+# What builds and launches the map kernel: its sources, the planner that sets
+# its launch (grid, LDS, residency), the ABI and the compiler flags.
+MAP_KERNEL_SOURCES = ["software_pipelining_amd/csrc/" + f for f in (
+    "tp_engine.hpp", "tp_internal.hpp", "tp_pipeline.hpp", "tp_map.hpp", "tp_map_inst.hip",
+    "tp_plan.cpp", "tp_api.cpp")] + ["include/tilepipe.h", "software_pipelining_amd/build.py"]
+
+
 def kernel_source_hash() -> str:
-    """Hash of the kernel sources: a stored hardware-counter reading is only
-    reported while it still describes the kernels being run."""
+    """Hash of what builds and launches the map kernel: a stored hardware-counter
+    reading is only reported while it still describes the kernel being run."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "software_pipelining_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
+    for name in MAP_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
