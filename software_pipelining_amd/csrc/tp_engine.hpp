@@ -84,7 +84,11 @@ __device__ __forceinline__ u32x4 sgpr_res(const BufferRes &r)
 //     before every buffer instruction;
 //   - an SALU write of M0 followed by an LDS-DMA load needs 1: the same nop;
 //   - a store of more than 8 bytes followed by a VALU write of its data VGPRs
-//     needs 1: "s_nop 0" right after every 16-byte store.
+//     needs 2 on this architecture family (the store reads its data late):
+//     "s_nop 1" right after every 16-byte store. With one wait state the
+//     compiler's next instruction may overwrite the first data register
+//     before the store has read it, and that dword of the chunk is stored
+//     wrong, now and then.
 
 // Cache-policy modifiers of the streaming loads and stores (compile-time).
 // Streamed data is touched once: loads are non-temporal, stores are
@@ -140,7 +144,7 @@ __device__ __forceinline__ void store_b128(const BufferRes &r, uint32_t voff, u3
 {
     asm volatile("s_nop 4\n\t"
                  "buffer_store_dwordx4 %0, %1, %2, 0 offen" TP_STORE_CPOL "\n\t"
-                 "s_nop 0"
+                 "s_nop 1"
                  :
                  : "v"(v), "v"(voff), "s"(sgpr_res(r))
                  : "memory");

@@ -9,7 +9,8 @@ code object built here and verify the rules those asm blocks must keep:
   it needs 5 (the compiler may rebuild a descriptor with v_readfirstlane right
   before the asm block), and an LDS-DMA load needs 1 after its M0 write;
 * every LDS-DMA load has its M0 written inside the same block;
-* every 16-byte store is followed by a wait state (store-data hazard);
+* every 16-byte store is followed by two wait states before a VALU may write
+  its data registers (store-data hazard);
 * no instruction touches memory without a range check (no global_, flat_ or
   scratch_ instructions) and nothing writes through the scalar cache;
 * on every path through a kernel's control flow, each LDS-DMA load has
@@ -116,11 +117,62 @@ def test_lds_dma_sets_m0_in_block(kernels):
                 assert insts[i - 2][0] == "s_mov_b32" and insts[i - 2][1][0] == "m0", (name, i)
 
 
-def test_wide_stores_followed_by_wait_state(kernels):
+def _vregs(tok: str):
+    m = re.match(r"v\[(\d+):(\d+)\]", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"v(\d+)$", tok)
+    return {int(m.group(1))} if m else set()
+
+
+def test_wide_stores_followed_by_two_wait_states(kernels):
+    # a store of more than 8 bytes reads its data VGPRs late: a VALU write of
+    # them needs 2 wait states after it on this architecture family
+    n = 0
     for name, insts in kernels.items():
-        for i, (op, _) in enumerate(insts):
-            if op in ("buffer_store_dwordx4", "buffer_store_dwordx3"):
-                assert insts[i + 1][0] == "s_nop", (name, i)
+        for i, (op, ops) in enumerate(insts):
+            if op not in ("buffer_store_dwordx4", "buffer_store_dwordx3"):
+                continue
+            n += 1
+            nxt_op, nxt_ops = insts[i + 1]
+            assert nxt_op == "s_nop" and int(nxt_ops[0], 0) >= 1, (name, i)
+    assert n > 1000
+
+
+def test_wide_store_data_hazard_scan():
+    # a rule of the hazard scan itself, checked on known sequences: the two
+    # s_nop 0 wait states before a VALU write of the data are counted as two
+    seq = [("buffer_store_dwordx4", ["v[4:7]", "v1", "s[0:3]", "0 offen"]),
+           ("s_nop", ["0"]), ("v_mov_b32_e32", ["v4", "s3"])]
+    assert _store_data_hazards(seq) == [0]
+    seq[1] = ("s_nop", ["1"])
+    assert _store_data_hazards(seq) == []
+
+
+def _store_data_hazards(insts):
+    """Indices of wide stores whose data VGPRs a VALU writes less than 2 wait
+    states later (linear order)."""
+    bad = []
+    for i, (op, ops) in enumerate(insts):
+        if op not in ("buffer_store_dwordx4", "buffer_store_dwordx3"):
+            continue
+        data, ws = _vregs(ops[0]), 0
+        for op2, ops2 in insts[i + 1:i + 4]:
+            if ws >= 2:
+                break
+            if op2 == "s_nop":
+                ws += int(ops2[0], 0) + 1
+                continue
+            if op2.startswith("v_") and ops2 and _vregs(ops2[0].split()[0]) & data:
+                bad.append(i)
+                break
+            ws += 1
+    return bad
+
+
+def test_no_wide_store_data_hazard(kernels):
+    for name, insts in kernels.items():
+        assert _store_data_hazards(insts) == [], name
 
 
 def test_no_unchecked_or_scalar_memory_writes(kernels):
