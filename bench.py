@@ -41,12 +41,13 @@ def parse():
     ap.add_argument("--tiles-per-block", type=int, default=0,
                     help="consecutive tiles per workgroup (0: the library default)")
     ap.add_argument("--quick", action="store_true", help="headline only: no sweep, no extra rows")
-    ap.add_argument("--mode", choices=("bench", "stages", "sweep", "occupancy", "map2d"),
+    ap.add_argument("--mode", choices=("bench", "stages", "sweep", "occupancy", "map2d", "align"),
                     default="bench",
-                    help="stages: only the maps at 1-4 stages; sweep: only the 24-point stage/tile "
+                    help="stages: only the maps at 1-4 stages; sweep: only the 36-point stage/tile "
                          "sweep (both for hardware-counter passes); occupancy: scale2 bandwidth "
                          "against the bound on resident workgroups per CU; map2d: only the 2-D "
-                         "map with its default box (for counter passes)")
+                         "map with its default box (for counter passes); align: scale2 bandwidth "
+                         "against the offsets of in and out from a 128-byte line, both policies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline")
@@ -165,9 +166,12 @@ def sampled_parity(x_host, y_dev, op, windows=16, width=4096, seed=0):
         got = y_dev[lo:hi].cpu().numpy()
         if not np.array_equal(got.view(np.uint32), exp.view(np.uint32)):
             return False
-    # the ragged end too
-    exp = oracle.pipelined_map(xs[n - 1000:], op, threads=1)
-    return bool(np.array_equal(y_dev[n - 1000:].cpu().numpy().view(np.uint32), exp.view(np.uint32)))
+    # the start and the ragged end too
+    for lo, hi in ((0, min(n, 1000)), (max(0, n - 1000), n)):
+        exp = oracle.pipelined_map(xs[lo:hi], op, threads=1)
+        if not np.array_equal(y_dev[lo:hi].cpu().numpy().view(np.uint32), exp.view(np.uint32)):
+            return False
+    return True
 
 
 def cpu_baseline(x_host, op, bytes_per_elem, seconds):
@@ -217,10 +221,14 @@ def stages_mode(args):
 
 
 def sweep_points():
-    """The stage/tile sweep of scale-by-2 over 2^28 floats: source offset 0 and
-    4 bytes (misaligned fallback) x tile 256/1024/4096 x stages 1-4, at the
-    library's run length."""
-    return [(off, T, S) for off in (0, 1) for T in (256, 1024, 4096) for S in (1, 2, 3, 4)]
+    """The stage/tile sweep of scale-by-2 over 2^28 floats: tile 256/1024/4096 x
+    stages 1-4 at the library's run length, with the source 16-byte aligned,
+    and at a 4-byte offset both with 16-byte loads (the library's default) and
+    with the pages' 4-byte fallback. Consecutive points never launch the same
+    kernel on the same grid, so counter passes can tell them apart by order."""
+    return ([(0, "realign", T, S) for T in (256, 1024, 4096) for S in (1, 2, 3, 4)] +
+            [(1, a, T, S) for a in ("realign", "words") for T in (256, 1024, 4096)
+             for S in (1, 2, 3, 4)])
 
 
 def sweep_mode(args):
@@ -235,11 +243,12 @@ def sweep_mode(args):
     xbuf[:n].copy_(workloads.uniform_pm1(n, seed=2))
     y = torch.empty(n, dtype=torch.float32, device=dev)
     gpu_warmup(lambda: tp.pipelined_map(xbuf[:n], y, "scale2", 256, 2, 0))
-    for off, T, S in sweep_points():
+    for off, align, T, S in sweep_points():
         xin = xbuf[off:off + n]
-        plan = tp.plan_map(xin.data_ptr(), y.data_ptr(), n, "scale2", T, S, 0)
-        per, _ = time_launches(lambda: tp.pipelined_map(xin, y, "scale2", T, S, 0), 1, args.steps)
-        log(f"sweep offset {4 * off}B tile {T} S{S} grid {plan.grid} threads {plan.threads} "
+        plan = tp.plan_map(xin.data_ptr(), y.data_ptr(), n, "scale2", T, S, 0, align=align)
+        per, _ = time_launches(lambda: tp.pipelined_map(xin, y, "scale2", T, S, 0, align=align), 1,
+                               args.steps)
+        log(f"sweep offset {4 * off}B {align} tile {T} S{S} grid {plan.grid} threads {plan.threads} "
             f"path {tp.Path(plan.path).name.lower()}: {median(per) * 1e3:.1f} us")
     torch.cuda.synchronize()
 
@@ -301,6 +310,39 @@ def occupancy_mode(args):
     torch.cuda.synchronize()
 
 
+def align_mode(args):
+    """scale2 over 2^28 with in and out at byte offsets from a 256-byte
+    boundary, under the library's realignment and under the pages' 4-byte
+    fallback, tiles 256 and 1024, 2 stages, in interleaved rounds."""
+    import torch
+    import software_pipelining_amd as tp
+    dev = torch.device("cuda:0")
+    n = 1 << 28
+    xb = torch.empty(n + 64, device=dev).uniform_(-1, 1)
+    yb = torch.empty(n + 64, device=dev)
+    if xb.data_ptr() % 256 or yb.data_ptr() % 256:
+        raise RuntimeError("the buffers must start on a 256-byte boundary")
+    cases = [(0, 0), (16, 16), (64, 64), (0, 16), (0, 64), (0, 128), (4, 0), (16, 0), (64, 0),
+             (0, 4), (4, 4), (12, 4)]
+    points = [(ci, co, a, t) for ci, co in cases for a in ("realign", "words") for t in (256, 1024)]
+    res = {p: [] for p in points}
+    gpu_warmup(lambda: tp.pipelined_map(xb[:n], yb[:n], "scale2", 256, 2, 0), 300)
+    for _ in range(3):
+        for ci, co, a, t in points:
+            x, y = xb[ci // 4:ci // 4 + n], yb[co // 4:co // 4 + n]
+            f = lambda: tp.pipelined_map(x, y, "scale2", t, 2, 0, align=a)
+            per, _ = time_launches(f, 2, args.steps)
+            res[(ci, co, a, t)].append(8 * n / (median(per) * 1e-3) / 1e9)
+    for ci, co in cases:
+        line = []
+        for a in ("realign", "words"):
+            plan = tp.plan_map(xb.data_ptr() + ci, yb.data_ptr() + co, n, "scale2", 256, 2, 0, align=a)
+            gb = " ".join(f"tile {t} {median(res[(ci, co, a, t)]):.0f}" for t in (256, 1024))
+            line.append(f"{a} (head {plan.head}, path {tp.Path(plan.path).name.lower()}) {gb}")
+        log(f"align in +{ci} B out +{co} B: " + " | ".join(line))
+    torch.cuda.synchronize()
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -319,6 +361,9 @@ def main():
         return
     if args.mode == "map2d":
         map2d_mode(args)
+        return
+    if args.mode == "align":
+        align_mode(args)
         return
 
     import numpy as np
@@ -443,22 +488,45 @@ def extra_rows(args, tp, workloads, torch, np, dev, x_host, xbuf, y):
     rows = {}
     n = x_host.numel()
 
-    # stage/tile sweep with the 4-byte source offset (misaligned fallback)
+    # stage/tile sweep, aligned and with a 4-byte source offset (16-byte loads at
+    # that offset, and the pages' 4-byte fallback)
     sweep = []
+    shifted = torch.cat([x_host[1:], torch.zeros(1)])[:n]
+    parity = True
     gpu_warmup(lambda: tp.pipelined_map(xbuf[:n], y, "scale2", 256, 2, 0))
-    for off, T, S in sweep_points():
+    for off, align, T, S in sweep_points():
         xin = xbuf[off:off + n]
-        p = tp.pipelined_map(xin, y, "scale2", T, S, 0)
-        per, _ = time_launches(lambda: tp.pipelined_map(xin, y, "scale2", T, S, 0), 2, 8)
+        f = lambda: tp.pipelined_map(xin, y, "scale2", T, S, 0, align=align)
+        p = f()
+        per, _ = time_launches(f, 2, 8)
         gbs = 8 * n / (median(per) * 1e-3) / 1e9
-        sweep.append({"src_offset_bytes": 4 * off, "tile": T, "stages": S,
+        sweep.append({"src_offset_bytes": 4 * off, "align": align, "tile": T, "stages": S,
                       "path": tp.Path(p).name.lower(), "GBs": round(gbs, 1),
                       "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1)})
+        if off and S == 4 and T == 1024:
+            parity &= bool(sampled_parity(shifted, y, "scale2"))
     log("sweep done")
-    # parity of the last (fallback) point
-    rows["sweep_parity_offset4"] = bool(sampled_parity(torch.cat([x_host[1:], torch.zeros(1)])[:n], y,
-                                                       "scale2"))
+    rows["sweep_parity_offset4"] = parity
     rows["scale2_sweep"] = sweep
+
+    # the output 4 bytes past a 128-byte boundary, the case the 4-byte fallback
+    # serves worst: realigned (the first 31 floats element-wise, then 16-byte
+    # stores that fill whole lines) against the pages' fallback
+    ybuf = torch.empty(n + 4, dtype=torch.float32, device=dev)
+    yout = ybuf[1:n + 1]
+    mis = {}
+    for align in ("realign", "words"):
+        f = lambda: tp.pipelined_map(xbuf[:n], yout, "scale2", 256, 2, 0, align=align)
+        p = f()
+        per, _ = time_launches(f, 2, 10)
+        gbs = 8 * n / (median(per) * 1e-3) / 1e9
+        mis[align] = {"path": tp.Path(p).name.lower(), "GBs": round(gbs, 1),
+                      "pct_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+                      "parity": bool(sampled_parity(x_host, yout, "scale2"))}
+    rows["scale2_output_offset4"] = dict(mis, workload="scale2 over 2^28 floats, tile 256, 2 stages, "
+                                                       "output 4 bytes past a 128-byte boundary")
+    log(f"output offset 4 B: {mis}")
+    del ybuf, yout
 
     # small double-buffered map: 2^24, tile 256, 2 stages, 64 tiles per workgroup
     ns = 1 << 24

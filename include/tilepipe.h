@@ -23,11 +23,20 @@
  *    launches nothing.
  *  - Alignment: float and chunk buffers must be 4-byte aligned
  *    (TP_ERR_MISALIGNED otherwise). A buffer that is 4- but not 16-byte
- *    aligned is not an error: it selects the element-wise (4-byte) fallback
- *    for that side of the copy, and the choice is reported through path_out
- *    (the pages' fallback is silent: "Asynchronous Data Movement", section
- *    "Alignment requirements"; here it is observable). Results never depend on
- *    the path.
+ *    aligned is not an error. The pages send such a copy down a slower
+ *    element-wise path ("Asynchronous Data Movement", section "Alignment
+ *    requirements"). The maps do not need to by default (TP_ALIGN_REALIGN):
+ *    gfx950 serves 16-byte global accesses at any 4-byte alignment, and the
+ *    1-D map moves the floats before out's first 128-byte boundary (at most
+ *    31) element-wise, so that its 16-byte stores fill whole 128-byte lines
+ *    (on MI355X a store stream that splits lines ran up to a fifth slower,
+ *    even 16-byte aligned). When out - in is 64 modulo 128 it starts at in's
+ *    first 128-byte boundary instead, which leaves the stores split at half
+ *    lines, the cheaper of the two splits. With TP_ALIGN_WORDS
+ *    the maps follow the pages' rule, and the row exchange and the chunk copy
+ *    always do: a side whose pointer is not 16-byte aligned moves 4-byte
+ *    words. The choice is reported through path_out (the pages' fallback is
+ *    silent; here it is observable). Results never depend on the path.
  *  - Aliasing: an output may be exactly the same buffer as the input (every
  *    unit is read into LDS before it is written). Any partial overlap between
  *    an output and another argument is TP_ERR_OVERLAP.
@@ -73,6 +82,14 @@ typedef enum tp_path {
     TP_PATH_SCALAR = 3
 } tp_path;
 
+/* How the maps move a buffer that is 4- but not 16-byte aligned. */
+typedef enum tp_align {
+    TP_ALIGN_REALIGN = 0, /* 16-byte accesses at any 4-byte alignment; the 1-D map moves
+                             the floats before out's first 128-byte boundary (in's when
+                             out - in is 64 mod 128) element-wise */
+    TP_ALIGN_WORDS = 1    /* the pages' rule: 4-byte words on a side not 16-byte aligned */
+} tp_align;
+
 /* How the waves of a map workgroup share the work ("Asynchronous Data
  * Movement", section "Barriers and pipelines": producer and consumer roles). */
 typedef enum tp_schedule {
@@ -97,6 +114,10 @@ typedef struct tp_plan {
                                 lds_bytes is padded up to bound residency */
     int32_t schedule;        /* tp_schedule (map); 0 for the other entry points */
     int32_t chunk_bytes;     /* bytes per chunk (chunk copy); 0 for the other entry points */
+    int32_t align;           /* tp_align (maps); 0 for the other entry points */
+    int32_t head;            /* 1-D map, TP_ALIGN_REALIGN: floats before the first 128-byte
+                                boundary of out (or of in, when out - in is 64 mod 128),
+                                0..31, moved element-wise; 0 otherwise */
 } tp_plan;
 
 /* Human-readable name of a tp_status value ("TP_OK", ...); never NULL. */
@@ -147,8 +168,13 @@ TP_API int tp_row_shift(const float *a, float *b, int64_t rows, void *stream, in
  * MI355X short runs dispatched in order keep the memory traffic of all
  * resident workgroups within a narrow window and stream fastest).
  * stages * tile_elems * 4 must fit the device's LDS per workgroup
- * (TP_ERR_LDS_BUDGET). out == in is allowed. The result does not depend on
- * tile_elems, stages, tiles_per_block or the path.
+ * (TP_ERR_LDS_BUDGET). out == in is allowed. Buffers off a 128-byte boundary
+ * are moved as TP_ALIGN_REALIGN describes: the floats before out's first
+ * 128-byte boundary (at most 31) are moved element-wise and the rest is tiled
+ * from there, so the 16-byte stores fill whole lines, while the loads are 16
+ * bytes at whatever 4-byte alignment in then has (in's boundary is taken
+ * instead when out - in is 64 modulo 128). The result does not depend
+ * on tile_elems, stages, tiles_per_block or the path.
  */
 TP_API int tp_pipelined_map(const float *in, float *out, int64_t n, int op,
                             int tile_elems, int stages, int tiles_per_block,
@@ -180,11 +206,15 @@ TP_API int tp_pipelined_map(const float *in, float *out, int64_t n, int op,
  * LDS, compute and store. One workgroup barrier per iteration publishes the
  * landed tile and frees the slot the loading wave refills next (two per
  * iteration with one stage). Other values: TP_ERR_INVALID_ARG.
+ * align: TP_ALIGN_REALIGN (what tp_pipelined_map does), or TP_ALIGN_WORDS:
+ * a side whose pointer is not 16-byte aligned moves 4-byte words, and the
+ * tiles start at in[0]. Other values: TP_ERR_INVALID_ARG.
  * The other arguments, errors and results are those of tp_pipelined_map.
  */
 TP_API int tp_pipelined_map_ex(const float *in, float *out, int64_t n, int op,
                                int tile_elems, int stages, int tiles_per_block,
-                               int resident_cap, int schedule, void *stream, int *path_out);
+                               int resident_cap, int schedule, int align, void *stream,
+                               int *path_out);
 
 /*
  * Strided 2-D map ("Asynchronous Data Movement", section "The Tensor Memory
@@ -200,9 +230,12 @@ TP_API int tp_pipelined_map_ex(const float *in, float *out, int64_t n, int op,
  * default of 2) through an LDS ring of `stages` slots, each box read by
  * LDS-DMA loads from row * stride + column. Elements of an edge box outside
  * the matrix are neither read nor written, and dst outside the window is not
- * touched. Each side uses 16-byte accesses when its pointer is 16-byte
- * aligned and its stride and cols are multiples of 4, else 4-byte accesses
- * (reported in path_out; bit 0 loads, bit 1 stores). The library's bound on
+ * touched. With align TP_ALIGN_REALIGN both sides use 16-byte accesses
+ * whenever cols is a multiple of 4, at any 4-byte alignment of the pointers
+ * and any strides; with TP_ALIGN_WORDS a side uses them only when its pointer
+ * is also 16-byte aligned and its stride a multiple of 4. Otherwise the side
+ * moves 4-byte words (reported in path_out; bit 0 loads, bit 1 stores). Other
+ * align values: TP_ERR_INVALID_ARG. The library's bound on
  * resident workgroups per CU (tp_pipelined_map_ex) applies. Errors:
  * TP_ERR_INVALID_ARG (bad shape, box, stages, a band of box_rows rows up to
  * the run's last column spanning more than 1 GiB on either side, or more than
@@ -214,7 +247,8 @@ TP_API int tp_pipelined_map_ex(const float *in, float *out, int64_t n, int op,
  */
 TP_API int tp_map_2d(const float *src, int64_t src_stride, float *dst, int64_t dst_stride,
                      int64_t rows, int64_t cols, int op, int box_rows, int box_cols,
-                     int stages, int boxes_per_block, void *stream, int *path_out);
+                     int stages, int boxes_per_block, int align, void *stream,
+                     int *path_out);
 
 /*
  * Predicated 16-byte chunk copy ("Asynchronous Copies", section "A
@@ -263,12 +297,12 @@ TP_API int tp_plan_row_shift(const void *a, const void *b, int64_t rows,
                              int64_t lds_budget, tp_plan *plan);
 TP_API int tp_plan_pipelined_map(const void *in, const void *out, int64_t n, int op,
                                  int tile_elems, int stages, int tiles_per_block,
-                                 int resident_cap, int schedule, int64_t lds_budget,
-                                 tp_plan *plan);
+                                 int resident_cap, int schedule, int align,
+                                 int64_t lds_budget, tp_plan *plan);
 TP_API int tp_plan_map_2d(const void *src, int64_t src_stride, const void *dst,
                           int64_t dst_stride, int64_t rows, int64_t cols, int op, int box_rows,
-                          int box_cols, int stages, int boxes_per_block, int64_t lds_budget,
-                          tp_plan *plan);
+                          int box_cols, int stages, int boxes_per_block, int align,
+                          int64_t lds_budget, tp_plan *plan);
 TP_API int tp_plan_chunk_copy(const void *src, const void *dst, int64_t n_chunks,
                               int chunk_bytes, const void *pred, const void *src_size,
                               const void *ignore_src, int stages, int tiles_per_block,

@@ -6,12 +6,12 @@ thin ctypes binding; it loads the library on first use and raises if it has not
 been built; there is no CPU fallback.
 """
 from .tilepipe import (  # noqa: F401
-    TilepipeError, Path, Plan, Schedule, chunk_copy, device_check, lds_budget, library_path,
+    Align, TilepipeError, Path, Plan, Schedule, chunk_copy, device_check, lds_budget, library_path,
     map_2d, pipelined_map, plan_chunk_copy, plan_map, plan_map_2d, plan_row_shift, row_shift,
 )
 
 __all__ = [
-    "TilepipeError", "Path", "Plan", "Schedule", "chunk_copy", "device_check", "lds_budget",
+    "Align", "TilepipeError", "Path", "Plan", "Schedule", "chunk_copy", "device_check", "lds_budget",
     "library_path", "map_2d", "pipelined_map", "plan_chunk_copy", "plan_map", "plan_map_2d",
     "plan_row_shift", "row_shift",
 ]

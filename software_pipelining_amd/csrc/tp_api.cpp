@@ -168,20 +168,20 @@ TP_API int tp_plan_row_shift(const void *a, const void *b, int64_t rows, int64_t
 
 TP_API int tp_plan_pipelined_map(const void *in, const void *out, int64_t n, int op,
                                  int tile_elems, int stages, int tiles_per_block,
-                                 int resident_cap, int schedule, int64_t lds_budget,
-                                 tp_plan *plan)
+                                 int resident_cap, int schedule, int align,
+                                 int64_t lds_budget, tp_plan *plan)
 {
     return tp::plan_map((uintptr_t)in, (uintptr_t)out, n, op, tile_elems, stages, tiles_per_block,
-                        resident_cap, schedule, lds_budget, plan);
+                        resident_cap, schedule, align, lds_budget, plan);
 }
 
 TP_API int tp_plan_map_2d(const void *src, int64_t src_stride, const void *dst,
                           int64_t dst_stride, int64_t rows, int64_t cols, int op, int box_rows,
-                          int box_cols, int stages, int boxes_per_block, int64_t lds_budget,
-                          tp_plan *plan)
+                          int box_cols, int stages, int boxes_per_block, int align,
+                          int64_t lds_budget, tp_plan *plan)
 {
     return tp::plan_map_2d((uintptr_t)src, src_stride, (uintptr_t)dst, dst_stride, rows, cols, op,
-                           box_rows, box_cols, stages, boxes_per_block, lds_budget, plan);
+                           box_rows, box_cols, stages, boxes_per_block, align, lds_budget, plan);
 }
 
 TP_API int tp_plan_chunk_copy(const void *src, const void *dst, int64_t n_chunks,
@@ -217,16 +217,16 @@ TP_API int tp_pipelined_map(const float *in, float *out, int64_t n, int op, int 
                             int stages, int tiles_per_block, void *stream, int *path_out)
 {
     return tp_pipelined_map_ex(in, out, n, op, tile_elems, stages, tiles_per_block, 0,
-                               TP_SCHED_UNIFORM, stream, path_out);
+                               TP_SCHED_UNIFORM, TP_ALIGN_REALIGN, stream, path_out);
 }
 
 TP_API int tp_pipelined_map_ex(const float *in, float *out, int64_t n, int op, int tile_elems,
                                int stages, int tiles_per_block, int resident_cap, int schedule,
-                               void *stream, int *path_out)
+                               int align, void *stream, int *path_out)
 {
     tp_plan plan;
     int st = tp::plan_map((uintptr_t)in, (uintptr_t)out, n, op, tile_elems, stages,
-                          tiles_per_block, resident_cap, schedule, kNoBudget, &plan);
+                          tiles_per_block, resident_cap, schedule, align, kNoBudget, &plan);
     if (st != TP_OK)
         return st;
     if (path_out)
@@ -239,15 +239,16 @@ TP_API int tp_pipelined_map_ex(const float *in, float *out, int64_t n, int op, i
     // again with the device's budget: the ring must fit, and the LDS reserved
     // to bound residency never exceeds it
     st = tp::plan_map((uintptr_t)in, (uintptr_t)out, n, op, tile_elems, stages, tiles_per_block,
-                      resident_cap, schedule, lds, &plan);
+                      resident_cap, schedule, align, lds, &plan);
     if (st != TP_OK)
         return st;
     tp::MapParams p;
     memset(&p, 0, sizeof p);
-    p.in = in;
-    p.out = out;
-    p.n = n;
-    p.n_main = n & ~int64_t(3);
+    p.in = in + plan.head;        // the tiled body
+    p.out = out + plan.head;
+    p.n = n - plan.head;
+    p.n_main = p.n & ~int64_t(3);
+    p.head = plan.head;
     p.tiles_per_block = plan.tiles_per_block;
     tp::horner32_coefficients(p.coef);
     return finish_launch(launch_map(plan, p, op, stream));
@@ -255,11 +256,12 @@ TP_API int tp_pipelined_map_ex(const float *in, float *out, int64_t n, int op, i
 
 TP_API int tp_map_2d(const float *src, int64_t src_stride, float *dst, int64_t dst_stride,
                      int64_t rows, int64_t cols, int op, int box_rows, int box_cols, int stages,
-                     int boxes_per_block, void *stream, int *path_out)
+                     int boxes_per_block, int align, void *stream, int *path_out)
 {
     tp_plan plan;
     int st = tp::plan_map_2d((uintptr_t)src, src_stride, (uintptr_t)dst, dst_stride, rows, cols,
-                             op, box_rows, box_cols, stages, boxes_per_block, kNoBudget, &plan);
+                             op, box_rows, box_cols, stages, boxes_per_block, align, kNoBudget,
+                             &plan);
     if (st != TP_OK)
         return st;
     if (path_out)
@@ -270,7 +272,7 @@ TP_API int tp_map_2d(const float *src, int64_t src_stride, float *dst, int64_t d
     if ((st = current_device(&lds)) != TP_OK)
         return st;
     st = tp::plan_map_2d((uintptr_t)src, src_stride, (uintptr_t)dst, dst_stride, rows, cols, op,
-                         box_rows, box_cols, stages, boxes_per_block, lds, &plan);
+                         box_rows, box_cols, stages, boxes_per_block, align, lds, &plan);
     if (st != TP_OK)
         return st;
     tp::Map2dParams p;

@@ -21,7 +21,13 @@ constexpr int kMaxTilesPerBlock = 65536;
 constexpr int kMaxRowShiftRows = 1024;
 constexpr int kChunkTile = 256;            // chunks per tile of the chunk copy (one per lane)
 constexpr int kChunkMetaArrays = 3;        // pred, src_size, ignore_src
-constexpr int kMapTailLdsBytes = 256;      // LDS area for the final partial 16-byte chunk
+constexpr int kMapEdgeLdsBytes = 256;      // LDS area of the floats outside the whole 16-byte chunks
+// The 1-D map's tiled body starts at a boundary of this many bytes (the L2
+// line) of out, or of in when out then sits on a half-line boundary. On
+// MI355X a stream of 16-byte stores that splits lines ran up to a fifth
+// slower (1-2 % when split at half lines), a stream of loads that does up to
+// 4 % slower.
+constexpr int kRealignBytes = 128;
 constexpr int kVmcntMax = 63;              // vmcnt is a 6-bit counter on gfx9-family parts
 constexpr int64_t kMaxMapElems = int64_t(1) << 40;
 constexpr int64_t kMaxChunks = int64_t(1) << 36;
@@ -87,13 +93,15 @@ TP_HD constexpr bool map_wave_local(bool load_x4, bool store_x4)
     return load_x4 == store_x4;
 }
 
+// The tiled body of a 1-D map starts at in/out; `head` floats just before it
+// (when the output was realigned to 16 bytes) belong to the problem too.
 struct MapParams {
-    const float *in;
+    const float *in;         // first float of the body
     float *out;
-    int64_t n_main;          // elements in whole 16-byte chunks: n rounded down to a multiple of 4
-    int64_t n;               // all elements; [n_main, n) is the final partial chunk
+    int64_t n_main;          // body elements in whole 16-byte chunks: n rounded down to a multiple of 4
+    int64_t n;               // body elements; [n_main, n) is the final partial chunk
     int32_t tiles_per_block; // consecutive tiles per workgroup
-    int32_t pad;
+    int32_t head;            // 0..31 floats at in[-head .. -1] / out[-head .. -1]
     float coef[32];          // Horner coefficients (used by TP_OP_HORNER32 only)
 };
 
@@ -168,8 +176,8 @@ struct RowShiftParams {
 // Pure host code (no HIP): argument validation and launch geometry.
 int plan_row_shift(uintptr_t a, uintptr_t b, int64_t rows, int64_t lds_budget, tp_plan *plan);
 int plan_map(uintptr_t in, uintptr_t out, int64_t n, int op, int tile_elems, int stages,
-             int tiles_per_block, int resident_cap, int schedule, int64_t lds_budget,
-             tp_plan *plan);
+             int tiles_per_block, int resident_cap, int schedule, int align,
+             int64_t lds_budget, tp_plan *plan);
 // The library's residency bound for a map launch (0: none); see tp_pipelined_map_ex.
 int map_policy_resident_cap(int op, int tile_elems, int stages, int tiles_per_block, int waves);
 // Box of a 2-D map when the caller passes 0 x 0: 1024 floats, as wide as the
@@ -178,7 +186,7 @@ int map_policy_resident_cap(int op, int tile_elems, int stages, int tiles_per_bl
 void map2d_resolve_box(int64_t cols, int *box_rows, int *box_cols);
 int plan_map_2d(uintptr_t src, int64_t src_stride, uintptr_t dst, int64_t dst_stride,
                 int64_t rows, int64_t cols, int op, int box_rows, int box_cols, int stages,
-                int tiles_per_block, int64_t lds_budget, tp_plan *plan);
+                int tiles_per_block, int align, int64_t lds_budget, tp_plan *plan);
 int plan_chunk_copy(uintptr_t src, uintptr_t dst, int64_t n_chunks, int chunk_bytes,
                     uintptr_t pred, uintptr_t src_size, uintptr_t ignore_src, int stages,
                     int tiles_per_block, int64_t lds_budget, tp_plan *plan);

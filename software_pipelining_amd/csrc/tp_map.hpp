@@ -10,7 +10,9 @@
 // contiguously in its LDS slot. With the 16-byte path, lane `tid` moves chunk
 // i*threads + tid (i < L) of the tile; with the 4-byte fallback it moves float
 // i*threads + tid (i < 4L). Loads and stores choose their width
-// independently from the alignment of `in` and `out`.
+// independently. The 16-byte accesses need only 4-byte alignment; the host
+// starts the body at out's first 128-byte line boundary, so its stores fill
+// whole lines.
 #pragma once
 
 #include <array>
@@ -69,6 +71,23 @@ struct MapOp<TP_OP_HORNER32> {
 };
 
 __device__ __forceinline__ uint32_t f2u(float x) { return __builtin_bit_cast(uint32_t, x); }
+
+// `count` (at most 64) floats outside the body's whole 16-byte chunks, moved
+// element-wise by one wave: lane l loads src[l] into the LDS area at byte
+// address `area` (lanes past `count` are out of range: they move nothing and
+// store nothing), waits for its own copy, applies the op and stores dst[l].
+template <int OP>
+__device__ __forceinline__ void map_edge(const float *src, float *dst, uint32_t count, uint32_t area,
+                                         const uint8_t *area_ptr, uint32_t lane, const float *coef)
+{
+    const BufferRes ri = make_buffer_res(src, count * 4);
+    const BufferRes ro = make_buffer_res(dst, count * 4);
+    dma_b32(ri, lane * 4, uniform(area));
+    vm_wait<0>();
+    float v[1] = {*reinterpret_cast<const float *>(area_ptr + lane * 4)};
+    MapOp<OP>::apply(v, coef);
+    store_b32(ro, lane * 4, f2u(v[0]));
+}
 
 template <int OP, int S, int L, bool LX4, bool SX4>
 __global__ void __launch_bounds__(256) map_kernel(MapParams p)
@@ -139,22 +158,21 @@ __global__ void __launch_bounds__(256) map_kernel(MapParams p)
     if (cnt > 0)
         pipeline_run<S, LD, ST, map_wave_local(LX4, SX4)>(cnt, ring, tile_bytes, issue, consume);
 
-    // The final partial 16-byte chunk (n not a multiple of 4): at most three
-    // floats, moved element-wise by the first wave of the last workgroup
-    // through an LDS area of its own.
-    if (p.n > p.n_main && b == gridDim.x - 1 && wave_first == 0) {
-        const uint32_t tail = (uint32_t)(p.n - p.n_main);
-        const BufferRes ti = make_buffer_res(p.in + p.n_main, tail * 4);
-        const BufferRes to = make_buffer_res(p.out + p.n_main, tail * 4);
-        const uint32_t tail_off = S * tile_bytes;
-        dma_b32(ti, tid * 4, uniform(ring + tail_off));
-        vm_wait<0>();
-        float v[1] = {*reinterpret_cast<const float *>(lds + tail_off + tid * 4)};
-        MapOp<OP>::apply(v, p.coef);
-        store_b32(to, tid * 4, f2u(v[0]));
+    // The floats outside the body's whole 16-byte chunks, moved element-wise
+    // by the first wave through an LDS area of its own: the 0-31 floats before
+    // the body (workgroup 0) and the body's final partial chunk (the last
+    // workgroup; both when there is one workgroup).
+    if (wave_first == 0) {
+        const uint32_t edge_off = S * tile_bytes;
+        if (b == 0 && p.head > 0)
+            map_edge<OP>(p.in - p.head, p.out - p.head, (uint32_t)p.head, ring + edge_off,
+                         lds + edge_off, tid, p.coef);
+        if (b == gridDim.x - 1 && p.n > p.n_main)
+            map_edge<OP>(p.in + p.n_main, p.out + p.n_main, (uint32_t)(p.n - p.n_main),
+                         ring + edge_off, lds + edge_off, tid, p.coef);
     }
     // No copy into LDS is in flight here: pipeline_run retires its last load
-    // before it returns, and the tail waits for its own.
+    // before it returns, and each edge pass waits for its own.
 }
 
 // Kernel table of one op over stage counts SLO..SHI:

@@ -145,19 +145,17 @@ __global__ void __launch_bounds__(320) map_split_kernel(MapParams p)
         }
     }
 
-    // The final partial 16-byte chunk (n not a multiple of 4): at most three
-    // floats, moved by the first consumer wave of the last workgroup through an
-    // LDS area of its own; it waits for its own copy before reading it.
-    if (p.n > p.n_main && b == gridDim.x - 1 && wave_first == 0) {
-        const uint32_t tail = (uint32_t)(p.n - p.n_main);
-        const BufferRes ti = make_buffer_res(p.in + p.n_main, tail * 4);
-        const BufferRes to = make_buffer_res(p.out + p.n_main, tail * 4);
-        const uint32_t tail_off = S * tile_bytes;
-        dma_b32(ti, tid * 4, uniform(ring + tail_off));
-        vm_wait<0>();
-        float v[1] = {*reinterpret_cast<const float *>(lds + tail_off + tid * 4)};
-        MapOp<OP>::apply(v, p.coef);
-        store_b32(to, tid * 4, f2u(v[0]));
+    // The floats outside the body's whole 16-byte chunks (before the body and
+    // its final partial chunk), moved by the first consumer wave as in the
+    // uniform schedule.
+    if (wave_first == 0) {
+        const uint32_t edge_off = S * tile_bytes;
+        if (b == 0 && p.head > 0)
+            map_edge<OP>(p.in - p.head, p.out - p.head, (uint32_t)p.head, ring + edge_off,
+                         lds + edge_off, tid, p.coef);
+        if (b == gridDim.x - 1 && p.n > p.n_main)
+            map_edge<OP>(p.in + p.n_main, p.out + p.n_main, (uint32_t)(p.n - p.n_main),
+                         ring + edge_off, lds + edge_off, tid, p.coef);
     }
 }
 

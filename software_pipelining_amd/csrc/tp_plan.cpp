@@ -118,10 +118,12 @@ int plan_row_shift(uintptr_t a, uintptr_t b, int64_t rows, int64_t lds_budget, t
 }
 
 int plan_map(uintptr_t in, uintptr_t out, int64_t n, int op, int tile_elems, int stages,
-             int tiles_per_block, int resident_cap, int schedule, int64_t lds_budget,
-             tp_plan *plan)
+             int tiles_per_block, int resident_cap, int schedule, int align,
+             int64_t lds_budget, tp_plan *plan)
 {
     if (resident_cap < -1 || (schedule != TP_SCHED_UNIFORM && schedule != TP_SCHED_ROLE_SPLIT))
+        return TP_ERR_INVALID_ARG;
+    if (align != TP_ALIGN_REALIGN && align != TP_ALIGN_WORDS)
         return TP_ERR_INVALID_ARG;
     if (n < 0 || n > kMaxMapElems)
         return TP_ERR_INVALID_ARG;
@@ -145,8 +147,9 @@ int plan_map(uintptr_t in, uintptr_t out, int64_t n, int op, int tile_elems, int
     p.threads = g.threads + (schedule == TP_SCHED_ROLE_SPLIT ? 64 : 0);
     p.lane_chunks = g.lane_chunks;
     p.schedule = schedule;
+    p.align = align;
     p.tiles_per_block = tpb;
-    p.ring_bytes = stages * tile_elems * 4 + kMapTailLdsBytes;
+    p.ring_bytes = stages * tile_elems * 4 + kMapEdgeLdsBytes;
     if (n > 0) {
         if (!in || !out)
             return TP_ERR_INVALID_ARG;
@@ -164,7 +167,20 @@ int plan_map(uintptr_t in, uintptr_t out, int64_t n, int op, int tile_elems, int
     p.resident_cap = cap >= kMaxWavesPerCu / waves ? 0 : (cap < 0 ? 0 : cap);
     p.lds_bytes = p.resident_cap ? reserve_for_cap(p.ring_bytes, p.resident_cap, lds_budget)
                                  : p.ring_bytes;
-    p.path = n > 0 ? path_bits(in, out) : TP_PATH_X4;
+    p.path = TP_PATH_X4;
+    if (n > 0 && align == TP_ALIGN_WORDS) {
+        p.path = path_bits(in, out);
+    } else if (n > 0) {
+        // 16-byte loads at any 4-byte alignment. The body starts at out's first
+        // line boundary, so its stores fill whole lines; or at in's, when that
+        // puts out on a half-line boundary: a store stream split at half lines
+        // cost less than a load stream split inside lines
+        const uintptr_t skew = (out - in) % kRealignBytes;
+        const uintptr_t anchor = skew == kRealignBytes / 2 ? in : out;
+        const int64_t to_boundary =
+            (int64_t)((kRealignBytes - anchor % kRealignBytes) % kRealignBytes / 4);
+        p.head = (int32_t)(to_boundary < n ? to_boundary : n);
+    }
     const bool load_x4 = !(p.path & TP_PATH_SCALAR_LOAD);
     const bool store_x4 = !(p.path & TP_PATH_SCALAR_STORE);
     if (schedule == TP_SCHED_ROLE_SPLIT) {
@@ -176,7 +192,7 @@ int plan_map(uintptr_t in, uintptr_t out, int64_t n, int op, int tile_elems, int
                                          map_stores_per_tile(store_x4, g.lane_chunks), stages,
                                          map_wave_local(load_x4, store_x4));
     }
-    const int64_t n_main = n & ~int64_t(3);
+    const int64_t n_main = (n - p.head) & ~int64_t(3);   // the body's whole 16-byte chunks
     p.num_tiles = ceil_div(n_main, tile_elems);
     p.grid = n == 0 ? 0 : (p.num_tiles == 0 ? 1 : ceil_div(p.num_tiles, tpb));
     if (p.grid > INT32_MAX)        // more workgroups than one launch can name
@@ -199,8 +215,10 @@ void map2d_resolve_box(int64_t cols, int *box_rows, int *box_cols)
 
 int plan_map_2d(uintptr_t src, int64_t src_stride, uintptr_t dst, int64_t dst_stride,
                 int64_t rows, int64_t cols, int op, int box_rows, int box_cols, int stages,
-                int tiles_per_block, int64_t lds_budget, tp_plan *plan)
+                int tiles_per_block, int align, int64_t lds_budget, tp_plan *plan)
 {
+    if (align != TP_ALIGN_REALIGN && align != TP_ALIGN_WORDS)
+        return TP_ERR_INVALID_ARG;
     map2d_resolve_box(cols, &box_rows, &box_cols);
     if (rows < 0 || cols < 0 || rows > kMaxMapElems || cols > kMaxMapElems)
         return TP_ERR_INVALID_ARG;
@@ -225,6 +243,7 @@ int plan_map_2d(uintptr_t src, int64_t src_stride, uintptr_t dst, int64_t dst_st
     p.tiles_per_block = tpb;
     p.ring_bytes = (int32_t)(stages * tile * 4);
     p.schedule = TP_SCHED_UNIFORM;
+    p.align = align;
     if (p.ring_bytes > lds_budget)
         return TP_ERR_LDS_BUDGET;
     p.lds_bytes = p.ring_bytes;
@@ -254,8 +273,11 @@ int plan_map_2d(uintptr_t src, int64_t src_stride, uintptr_t dst, int64_t dst_st
             return TP_ERR_INVALID_ARG;
         p.num_tiles = bands * boxes_per_band;
         p.grid = bands * runs;
-        const bool load_x4 = src % 16 == 0 && src_stride % 4 == 0 && cols % 4 == 0;
-        const bool store_x4 = dst % 16 == 0 && dst_stride % 4 == 0 && cols % 4 == 0;
+        // a 16-byte chunk is 4 floats of one row: cols % 4 == 0 keeps every chunk
+        // inside its row; the pages' rule also wants it 16-byte aligned
+        const bool words = align == TP_ALIGN_WORDS;
+        const bool load_x4 = cols % 4 == 0 && (!words || (src % 16 == 0 && src_stride % 4 == 0));
+        const bool store_x4 = cols % 4 == 0 && (!words || (dst % 16 == 0 && dst_stride % 4 == 0));
         p.path = (load_x4 ? 0 : TP_PATH_SCALAR_LOAD) | (store_x4 ? 0 : TP_PATH_SCALAR_STORE);
     }
     const bool load_x4 = !(p.path & TP_PATH_SCALAR_LOAD);

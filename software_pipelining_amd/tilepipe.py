@@ -32,6 +32,22 @@ class Schedule(enum.IntEnum):
     ROLE_SPLIT = 1
 
 
+class Align(enum.IntEnum):
+    REALIGN = 0
+    WORDS = 1
+
+
+def _align(align) -> int:
+    """tp_align value for the C ABI; out-of-range integers pass through so the
+    library reports them."""
+    if isinstance(align, str):
+        try:
+            return int(Align[align.upper()])
+        except KeyError:
+            raise ValueError(f"unknown align {align!r}; expected 'realign' or 'words'")
+    return int(align)
+
+
 def _schedule(schedule) -> int:
     """Schedule value for the C ABI; out-of-range integers pass through so the
     library reports them."""
@@ -61,7 +77,8 @@ class _CPlan(ctypes.Structure):
                 ("lds_bytes", ctypes.c_int32), ("wait_steady", ctypes.c_int32),
                 ("num_tiles", ctypes.c_int64), ("grid", ctypes.c_int64),
                 ("ring_bytes", ctypes.c_int32), ("resident_cap", ctypes.c_int32),
-                ("schedule", ctypes.c_int32), ("chunk_bytes", ctypes.c_int32)]
+                ("schedule", ctypes.c_int32), ("chunk_bytes", ctypes.c_int32),
+                ("align", ctypes.c_int32), ("head", ctypes.c_int32)]
 
 
 @dataclass(frozen=True)
@@ -80,6 +97,8 @@ class Plan:
     resident_cap: int
     schedule: "Schedule"
     chunk_bytes: int
+    align: "Align"
+    head: int
 
 
 _lib = None
@@ -109,14 +128,15 @@ def _load():
         "tp_device_lds_budget": ([i32, ctypes.POINTER(ctypes.c_int64)], i32),
         "tp_row_shift": ([vp, vp, i64, vp, ip], i32),
         "tp_pipelined_map": ([vp, vp, i64, i32, i32, i32, i32, vp, ip], i32),
-        "tp_pipelined_map_ex": ([vp, vp, i64, i32, i32, i32, i32, i32, i32, vp, ip], i32),
+        "tp_pipelined_map_ex": ([vp, vp, i64, i32, i32, i32, i32, i32, i32, i32, vp, ip], i32),
         "tp_chunk_copy": ([vp, vp, i64, vp, vp, vp, i32, i32, vp, ip], i32),
         "tp_chunk_copy_ex": ([vp, vp, i64, i32, vp, vp, vp, i32, i32, vp, ip], i32),
         "tp_plan_row_shift": ([vp, vp, i64, i64, pp], i32),
-        "tp_plan_pipelined_map": ([vp, vp, i64, i32, i32, i32, i32, i32, i32, i64, pp], i32),
+        "tp_plan_pipelined_map": ([vp, vp, i64, i32, i32, i32, i32, i32, i32, i32, i64, pp], i32),
         "tp_plan_chunk_copy": ([vp, vp, i64, i32, vp, vp, vp, i32, i32, i64, pp], i32),
-        "tp_map_2d": ([vp, i64, vp, i64, i64, i64, i32, i32, i32, i32, i32, vp, ip], i32),
-        "tp_plan_map_2d": ([vp, i64, vp, i64, i64, i64, i32, i32, i32, i32, i32, i64, pp], i32),
+        "tp_map_2d": ([vp, i64, vp, i64, i64, i64, i32, i32, i32, i32, i32, i32, vp, ip], i32),
+        "tp_plan_map_2d": ([vp, i64, vp, i64, i64, i64, i32, i32, i32, i32, i32, i32, i64, pp],
+                           i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -192,14 +212,17 @@ def row_shift(a, b=None, stream=None) -> Path:
 
 def pipelined_map(x, y=None, op: str = "scale2", tile_elems: int = 1024, stages: int = 2,
                   tiles_per_block: int = 0, stream=None, resident_cap: int = 0,
-                  schedule: "Schedule | str" = "uniform") -> Path:
+                  schedule: "Schedule | str" = "uniform",
+                  align: "Align | str" = "realign") -> Path:
     """y[i] = op(x[i]) for float32 GPU tensors (any shape, contiguous).
 
     Each workgroup streams tiles_per_block consecutive tiles (0: the
     library default of 2). resident_cap bounds the workgroups per CU
     (0: the library's policy, -1: no bound, k: about k). schedule "uniform"
     (every wave loads its own part) or "role_split" (one wave loads, the
-    others compute)."""
+    others compute). align "realign" (16-byte accesses at any 4-byte
+    alignment, stores aligned to y) or "words" (4-byte words on a side that
+    is not 16-byte aligned)."""
     import torch
     if op not in OPS:
         raise ValueError(f"unknown op {op!r}; expected one of {sorted(OPS)}")
@@ -215,8 +238,8 @@ def pipelined_map(x, y=None, op: str = "scale2", tile_elems: int = 1024, stages:
         st = _load().tp_pipelined_map_ex(ctypes.c_void_p(x.data_ptr()),
                                          ctypes.c_void_p(y.data_ptr()), x.numel(), OPS[op],
                                          tile_elems, stages, tiles_per_block, resident_cap,
-                                         _schedule(schedule), _stream_handle(x, stream),
-                                         ctypes.byref(path))
+                                         _schedule(schedule), _align(align),
+                                         _stream_handle(x, stream), ctypes.byref(path))
     _check(st, "tp_pipelined_map_ex")
     return Path(path.value)
 
@@ -231,10 +254,12 @@ def _row_stride(t, name: str) -> int:
 
 
 def map_2d(src, dst, op: str = "scale2", box_rows: int = 0, box_cols: int = 0,
-           stages: int = 2, boxes_per_block: int = 0, stream=None) -> Path:
+           stages: int = 2, boxes_per_block: int = 0, stream=None,
+           align: "Align | str" = "realign") -> Path:
     """dst[r, c] = op(src[r, c]) for two same-shape 2-D float32 GPU views with
     unit column stride (rows any number of elements apart). box 0 x 0: the
-    library's choice (1024 floats, as wide as the window allows)."""
+    library's choice (1024 floats, as wide as the window allows). align as
+    for pipelined_map."""
     import torch
     if op not in OPS:
         raise ValueError(f"unknown op {op!r}; expected one of {sorted(OPS)}")
@@ -250,7 +275,7 @@ def map_2d(src, dst, op: str = "scale2", box_rows: int = 0, box_cols: int = 0,
         st = _load().tp_map_2d(ctypes.c_void_p(src.data_ptr()), _row_stride(src, "src"),
                                ctypes.c_void_p(dst.data_ptr()), _row_stride(dst, "dst"),
                                rows, cols, OPS[op], box_rows, box_cols, stages, boxes_per_block,
-                               _stream_handle(src, stream), ctypes.byref(path))
+                               _align(align), _stream_handle(src, stream), ctypes.byref(path))
     _check(st, "tp_map_2d")
     return Path(path.value)
 
@@ -296,7 +321,8 @@ def _plan(status: int, cp: _CPlan, where: str) -> Plan:
     _check(status, where)
     return Plan(Path(cp.path), cp.stages, cp.tile_units, cp.threads, cp.lane_chunks,
                 cp.tiles_per_block, cp.lds_bytes, cp.wait_steady, cp.num_tiles, cp.grid,
-                cp.ring_bytes, cp.resident_cap, Schedule(cp.schedule), cp.chunk_bytes)
+                cp.ring_bytes, cp.resident_cap, Schedule(cp.schedule), cp.chunk_bytes,
+                Align(cp.align), cp.head)
 
 
 def plan_row_shift(a_ptr: int, b_ptr: int, rows: int, lds_budget: int = _NO_BUDGET) -> Plan:
@@ -308,23 +334,27 @@ def plan_row_shift(a_ptr: int, b_ptr: int, rows: int, lds_budget: int = _NO_BUDG
 
 def plan_map(in_ptr: int, out_ptr: int, n: int, op: str = "scale2", tile_elems: int = 1024,
              stages: int = 2, tiles_per_block: int = 0, lds_budget: int = _NO_BUDGET,
-             resident_cap: int = 0, schedule: "Schedule | str" = "uniform") -> Plan:
+             resident_cap: int = 0, schedule: "Schedule | str" = "uniform",
+             align: "Align | str" = "realign") -> Plan:
     cp = _CPlan()
     st = _load().tp_plan_pipelined_map(ctypes.c_void_p(in_ptr), ctypes.c_void_p(out_ptr), n,
                                        OPS.get(op, op if isinstance(op, int) else -1),
                                        tile_elems, stages, tiles_per_block, resident_cap,
-                                       _schedule(schedule), lds_budget, ctypes.byref(cp))
+                                       _schedule(schedule), _align(align), lds_budget,
+                                       ctypes.byref(cp))
     return _plan(st, cp, "tp_plan_pipelined_map")
 
 
 def plan_map_2d(src_ptr: int, src_stride: int, dst_ptr: int, dst_stride: int, rows: int,
                 cols: int, op: str = "scale2", box_rows: int = 0, box_cols: int = 0,
-                stages: int = 2, boxes_per_block: int = 0, lds_budget: int = _NO_BUDGET) -> Plan:
+                stages: int = 2, boxes_per_block: int = 0, lds_budget: int = _NO_BUDGET,
+                align: "Align | str" = "realign") -> Plan:
     cp = _CPlan()
     st = _load().tp_plan_map_2d(ctypes.c_void_p(src_ptr), src_stride, ctypes.c_void_p(dst_ptr),
                                 dst_stride, rows, cols,
                                 OPS.get(op, op if isinstance(op, int) else -1), box_rows,
-                                box_cols, stages, boxes_per_block, lds_budget, ctypes.byref(cp))
+                                box_cols, stages, boxes_per_block, _align(align), lds_budget,
+                                ctypes.byref(cp))
     return _plan(st, cp, "tp_plan_map_2d")
 
 

@@ -4,7 +4,8 @@ host inputs, in the launch configurations the benchmark times.
 1. row exchange of the 64x4 worked example;
 2. double-buffered scale-by-2, 2^24 floats, tile 256, 2 stages, 64 tiles/WG;
 3. stage/tile sweep of scale-by-2 over 2^28 floats, stages 1-4 x tiles
-   256/1024/4096, aligned and with a 4-byte source offset (fallback path);
+   256/1024/4096, aligned and with a 4-byte source offset (16-byte loads at that
+   offset, and the pages' 4-byte fallback);
 4. predicated chunk copy of 2^26 chunks;
 5. 32-step fmaf Horner chain over 2^27 floats, tile 1024, stages 1/2/4.
 """
@@ -51,12 +52,16 @@ def test_config3_stage_tile_sweep(cuda_device):
         xin = xbuf[off:off + n]
         for tile in (256, 1024, 4096):
             for stages in (1, 2, 3, 4):
-                for tpb in (0, 64):          # the library's run length (as benchmarked) and 64
+                # the library's run length (as benchmarked) and 64, and with the
+                # offset source both alignment policies
+                for tpb, align in ((0, "realign"), (64, "realign"), (0, "words")):
+                    if align == "words" and not off:
+                        continue
                     y.fill_(float("nan"))
-                    path = tp.pipelined_map(xin, y, "scale2", tile, stages, tpb)
-                    assert path == (tp.Path.SCALAR_LOAD if off else tp.Path.X4)
+                    path = tp.pipelined_map(xin, y, "scale2", tile, stages, tpb, align=align)
+                    assert path == (tp.Path.SCALAR_LOAD if align == "words" else tp.Path.X4)
                     assert_equal_on_device(y, exp, f"config 3 offset={4 * off}B tile={tile} "
-                                                   f"S={stages} T={tpb}")
+                                                   f"S={stages} T={tpb} {align}")
         del exp
 
 

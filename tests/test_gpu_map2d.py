@@ -1,7 +1,7 @@
 """GPU parity of tp_map_2d against the oracle (bit-exact), through the C ABI:
 windows of row-major matrices with row strides, every op, ragged edges that
-cut boxes, several box shapes, stages and runs, all four load/store paths and
-in-place use. The whole destination buffer is compared, so elements between
+cut boxes, several box shapes, stages and runs, both alignment policies (all
+four load/store paths) and in-place use. The whole destination buffer is compared, so elements between
 the rows and around the window must come back untouched ("Asynchronous Data
 Movement", section "The Tensor Memory Accelerator": a tile described by a
 base, a shape and strides)."""
@@ -35,7 +35,7 @@ def _view_t(buf, rows, cols, stride, off):
     return torch.as_strided(buf, (rows, cols), (stride, 1), GUARD + off)
 
 
-def _run(dev, op, rows, cols, ss, ds, soff, doff, box, stages, tpb, seed=0):
+def _run(dev, op, rows, cols, ss, ds, soff, doff, box, stages, tpb, seed=0, align="realign"):
     src_h = _buffers(rows, cols, ss, soff, seed=100 + seed)
     dst_h = np.full(_buffers(rows, cols, ds, doff, seed=1).size, SENTINEL, np.float32)
     expect = dst_h.copy()
@@ -44,9 +44,10 @@ def _run(dev, op, rows, cols, ss, ds, soff, doff, box, stages, tpb, seed=0):
     src = torch.from_numpy(src_h).to(dev)
     dst = torch.from_numpy(dst_h).to(dev)
     path = tp.map_2d(_view_t(src, rows, cols, ss, soff), _view_t(dst, rows, cols, ds, doff), op,
-                     box[0], box[1], stages, tpb)
+                     box[0], box[1], stages, tpb, align=align)
     got = dst.cpu().numpy()
-    what = f"{op} {rows}x{cols} ss={ss} ds={ds} off={soff},{doff} box={box} S={stages} T={tpb}"
+    what = (f"{op} {align} {rows}x{cols} ss={ss} ds={ds} off={soff},{doff} box={box} S={stages} "
+            f"T={tpb} path={int(path)}")
     bad = np.nonzero(got.view(np.uint32) != expect.view(np.uint32))[0]
     assert bad.size == 0, f"{what}: {bad.size} differ, first at {bad[:6].tolist()}"
     assert torch.equal(src.cpu(), torch.from_numpy(src_h)), what + ": source changed"
@@ -58,12 +59,16 @@ SHAPES = [(1, 1), (1, 300), (3, 5), (5, 4), (17, 300), (64, 256), (100, 1000), (
 BOXES = [(1, 256), (4, 256), (2, 512), (16, 64), (64, 4), (1, 8192), (8, 1024), (0, 0)]
 
 
+@pytest.mark.parametrize("align", ["realign", "words"])
 @pytest.mark.parametrize("op", ["scale2", "horner32", "copy"])
-def test_map_2d_parity_shapes_boxes(cuda_device, op):
+def test_map_2d_parity_shapes_boxes(cuda_device, op, align):
     for i, (rows, cols) in enumerate(SHAPES):
         for box in BOXES:
             for ss, ds in ((cols, cols), (cols + 4, cols + 12), (cols + 3, cols + 1)):
-                _run(cuda_device, op, rows, cols, ss, ds, 0, 0, box, 2, 0, seed=i)
+                path = _run(cuda_device, op, rows, cols, ss, ds, 0, 0, box, 2, 0, seed=i,
+                            align=align)
+                if align == "realign":
+                    assert path == (tp.Path.X4 if cols % 4 == 0 else tp.Path.SCALAR)
 
 
 @pytest.mark.parametrize("op", ["scale2", "copy"])
@@ -73,9 +78,10 @@ def test_map_2d_stages_runs_paths(cuda_device, op):
                              (0, 2, tp.Path.SCALAR_STORE), (3, 1, tp.Path.SCALAR)):
         for stages in (1, 2, 3, 4, 8):
             for tpb in (1, 2, 3, 64):
-                path = _run(cuda_device, op, rows, cols, cols + 4, cols + 8, soff, doff, (4, 256),
-                            stages, tpb)
-                assert path == want
+                for align in ("realign", "words"):
+                    path = _run(cuda_device, op, rows, cols, cols + 4, cols + 8, soff, doff,
+                                (4, 256), stages, tpb, align=align)
+                    assert path == (want if align == "words" else tp.Path.X4)
 
 
 def test_map_2d_in_place_and_empty(cuda_device):
@@ -105,4 +111,7 @@ def test_map_2d_errors(cuda_device):
     c = torch.as_strided(buf, (10, 100), (100, 1), 50_000)
     with pytest.raises(tp.TilepipeError) as e:
         tp.map_2d(a, c, "scale2", 3, 256)                       # box_rows not a power of two
+    assert e.value.status == 1
+    with pytest.raises(tp.TilepipeError) as e:
+        tp.map_2d(a, c, "scale2", align=3)
     assert e.value.status == 1

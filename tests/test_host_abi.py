@@ -83,10 +83,50 @@ def test_map_plan_tail_and_small_sizes():
 
 
 def test_map_plan_paths_follow_alignment():
-    assert tp.plan_map(A + 4, B, 100).path == tp.Path.SCALAR_LOAD
-    assert tp.plan_map(A, B + 8, 100).path == tp.Path.SCALAR_STORE
-    assert tp.plan_map(A + 12, B + 4, 100).path == tp.Path.SCALAR
-    assert tp.plan_map(A + 16, B + 32, 100).path == tp.Path.X4
+    # the pages' rule: 4-byte words on a side that is not 16-byte aligned
+    w = dict(align="words")
+    assert tp.plan_map(A + 4, B, 100, **w).path == tp.Path.SCALAR_LOAD
+    assert tp.plan_map(A, B + 8, 100, **w).path == tp.Path.SCALAR_STORE
+    assert tp.plan_map(A + 12, B + 4, 100, **w).path == tp.Path.SCALAR
+    assert tp.plan_map(A + 16, B + 32, 100, **w).path == tp.Path.X4
+    assert tp.plan_map(A + 12, B + 4, 100, **w).head == 0
+    assert tp.plan_map(A + 12, B + 4, 100, **w).align == tp.Align.WORDS
+
+
+def test_map_plan_realign():
+    # the default: 16-byte accesses at any 4-byte alignment, the tiled body
+    # starting at out's first 128-byte boundary (A and B are 128-byte aligned)
+    assert A % 128 == 0 and B % 128 == 0
+    n = 5000
+    for in_off in (0, 4, 8, 12, 64, 68):
+        for out_off in (0, 4, 8, 12, 16, 64, 124):
+            # out's boundary, or in's when out - in is 64 mod 128 (half-line stores)
+            anchor = in_off if (out_off - in_off) % 128 == 64 else out_off
+            head = (128 - anchor) % 128 // 4
+            p = tp.plan_map(A + in_off, B + out_off, n, tile_elems=1024, tiles_per_block=1)
+            assert (p.path, p.head, p.align) == (tp.Path.X4, head, tp.Align.REALIGN)
+            n_main = (n - head) // 4 * 4
+            assert (p.num_tiles, p.grid) == (-(-n_main // 1024), -(-n_main // 1024))
+    # fewer floats than the distance to the boundary: all of them are the head
+    for n in (1, 2, 3, 30, 31):
+        p = tp.plan_map(A, B + 4, n)
+        assert (p.head, p.num_tiles, p.grid) == (n, 0, 1)
+    p = tp.plan_map(A, B + 4, 32)
+    assert (p.head, p.num_tiles, p.grid) == (31, 0, 1)          # a 1-float tail
+    p = tp.plan_map(A, B + 4, 31 + 1024, tile_elems=1024, tiles_per_block=1)
+    assert (p.head, p.num_tiles, p.grid) == (31, 1, 1)
+    p = tp.plan_map(A, B + 120, 2 + 1023, tile_elems=1024, tiles_per_block=1)
+    assert (p.head, p.num_tiles, p.grid) == (2, 1, 1)           # 1020-float body, 3-float tail
+    assert tp.plan_map(A, B, 0).head == 0 and tp.plan_map(0, 0, 0, "scale2").grid == 0
+    # the realigned launch waits like the 16-byte path; in place keeps one head
+    assert tp.plan_map(A + 4, B + 4, 100, stages=2).wait_steady == 1 + 1
+    assert tp.plan_map(A + 8, A + 8, 100).head == 30
+    assert tp.plan_map(A, B + 64, 100).head == 0                  # stores at half lines
+    assert tp.plan_map(A + 4, B + 68, 100).head == 31             # in's boundary
+    assert tp.plan_map(B + 68, A + 4, 100).head == 15
+    assert tp.plan_map(A + 64, B, 100).head == 16                 # out - in = -64 = 64 mod 128
+    for bad in (2, -1):
+        assert _status(tp.plan_map, A, B, 10, align=bad) == 1
 
 
 def test_map_plan_wait_counts():
@@ -97,11 +137,13 @@ def test_map_plan_wait_counts():
     assert tp.plan_map(A, B, 100, stages=1).wait_steady == 0
     assert tp.plan_map(A, B, 100, stages=2).wait_steady == 1 + 1
     assert tp.plan_map(A, B, 100, stages=4, tile_elems=4096).wait_steady == 3 * 4 + 3 * 4
-    assert tp.plan_map(A + 4, B + 4, 100, stages=2, tile_elems=1024).wait_steady == 4 + 4
-    assert tp.plan_map(A + 4, B, 100, stages=1, tile_elems=1024).wait_steady == 0
-    assert tp.plan_map(A + 4, B, 100, stages=3, tile_elems=1024).wait_steady == 4 + 2
-    assert tp.plan_map(A, B + 4, 100, stages=2, tile_elems=2048).wait_steady == 0 + 8
-    assert tp.plan_map(A + 4, B + 4, 100, stages=8, tile_elems=8192).wait_steady == 63
+    assert tp.plan_map(A + 4, B + 4, 100, stages=2, tile_elems=1024,
+                       align="words").wait_steady == 4 + 4
+    w = dict(align="words")
+    assert tp.plan_map(A + 4, B, 100, stages=1, tile_elems=1024, **w).wait_steady == 0
+    assert tp.plan_map(A + 4, B, 100, stages=3, tile_elems=1024, **w).wait_steady == 4 + 2
+    assert tp.plan_map(A, B + 4, 100, stages=2, tile_elems=2048, **w).wait_steady == 0 + 8
+    assert tp.plan_map(A + 4, B + 4, 100, stages=8, tile_elems=8192, **w).wait_steady == 63
 
 
 @pytest.mark.parametrize("args,status", [
@@ -227,7 +269,8 @@ def test_map_role_split_plan():
             p = tp.plan_map(A, B, 1 << 20, "horner32", tile, S, 2, schedule="role_split")
             assert p.schedule == tp.Schedule.ROLE_SPLIT and p.threads == threads
             assert p.wait_steady == min(63, (S - 2) * per_tile) if S > 1 else p.wait_steady == 0
-            q = tp.plan_map(A + 4, B, 1 << 20, "horner32", tile, S, 2, schedule="role_split")
+            q = tp.plan_map(A + 4, B, 1 << 20, "horner32", tile, S, 2, schedule="role_split",
+                            align="words")
             assert q.wait_steady == (min(63, (S - 2) * 4 * per_tile) if S > 1 else 0)
             u = tp.plan_map(A, B, 1 << 20, "horner32", tile, S, 2)
             assert (u.schedule, u.threads) == (tp.Schedule.UNIFORM, threads - 64)
@@ -249,10 +292,18 @@ def test_map_2d_plan_geometry_and_paths():
     assert (p.num_tiles, p.grid) == (bands * boxes, bands * -(-boxes // 3))
     assert p.ring_bytes == 2 * 1024 * 4 and p.lds_bytes >= p.ring_bytes
     assert p.path == tp.Path.X4
-    assert tp.plan_map_2d(A + 4, 1000, B, 1024, 100, 1000).path == tp.Path.SCALAR_LOAD
-    assert tp.plan_map_2d(A, 1002, B, 1024, 100, 1000).path == tp.Path.SCALAR_LOAD   # stride
-    assert tp.plan_map_2d(A, 1000, B, 1026, 100, 1000).path == tp.Path.SCALAR_STORE
-    assert tp.plan_map_2d(A, 1000, B, 1024, 100, 998).path == tp.Path.SCALAR          # cols
+    # the pages' rule: 16-byte aligned pointer and a stride of whole chunks
+    w = dict(align="words")
+    assert tp.plan_map_2d(A + 4, 1000, B, 1024, 100, 1000, **w).path == tp.Path.SCALAR_LOAD
+    assert tp.plan_map_2d(A, 1002, B, 1024, 100, 1000, **w).path == tp.Path.SCALAR_LOAD   # stride
+    assert tp.plan_map_2d(A, 1000, B, 1026, 100, 1000, **w).path == tp.Path.SCALAR_STORE
+    assert tp.plan_map_2d(A, 1000, B, 1024, 100, 998, **w).path == tp.Path.SCALAR          # cols
+    # realign (the default): only cols decides
+    for src, ss, dst, ds in ((A + 4, 1000, B, 1024), (A, 1002, B, 1024), (A, 1000, B + 12, 1027)):
+        assert tp.plan_map_2d(src, ss, dst, ds, 100, 1000).path == tp.Path.X4
+        assert tp.plan_map_2d(src, ss, dst, ds, 100, 998).path == tp.Path.SCALAR
+    assert tp.plan_map_2d(A, 1000, B, 1024, 100, 1000).head == 0
+    assert _status(tp.plan_map_2d, A, 1000, B, 1024, 100, 1000, align=7) == 1
     for br, bc, threads, lanes in [(1, 256, 64, 1), (64, 4, 64, 1), (2, 4096, 256, 8), (16, 64, 256, 1)]:
         p = tp.plan_map_2d(A, 8192, B, 8192, 50, 5000, "copy", br, bc, 1, 1)
         assert (p.threads, p.lane_chunks) == (threads, lanes)
@@ -424,7 +475,16 @@ def test_header_is_plain_c():
     import tempfile
     with tempfile.TemporaryDirectory() as d:
         src = os.path.join(d, "t.c")
+        fields = [f for f, _ in tilepipe._CPlan._fields_]
         with open(src, "w") as f:
-            f.write('#include "tilepipe.h"\nint main(void){tp_plan p; (void)p; return TP_OK;}\n')
-        subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", f"-I{ROOT}/include", "-c", src,
-                        "-o", os.path.join(d, "t.o")], check=True)
+            f.write('#include <stddef.h>\n#include <stdio.h>\n#include "tilepipe.h"\n'
+                    'int main(void){printf("%zu", sizeof(tp_plan));'
+                    + "".join(f'printf(" %zu", offsetof(tp_plan, {n}));' for n in fields)
+                    + "return TP_OK;}\n")
+        exe = os.path.join(d, "t")
+        subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", f"-I{ROOT}/include", src, "-o", exe],
+                       check=True)
+        # the binding's mirror of tp_plan has the C struct's size and offsets
+        got = [int(v) for v in subprocess.run([exe], capture_output=True, text=True).stdout.split()]
+        assert got[0] == ctypes.sizeof(tilepipe._CPlan)
+        assert got[1:] == [getattr(tilepipe._CPlan, n).offset for n in fields]
