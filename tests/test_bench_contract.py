@@ -1,0 +1,70 @@
+"""Host-side checks of bench.py that need no GPU: the one-GPU contract, the
+algorithmic byte count of the chunk copy, and the ordering property the
+hardware-counter summaries rely on."""
+import importlib.util
+import os
+import subprocess
+import sys
+
+import software_pipelining_amd as tp
+from software_pipelining_amd import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_chunk_copy_algorithmic_bytes_brute_force():
+    # per chunk: 3 metadata bytes, the kept source prefix of a written chunk,
+    # and 16 bytes written when pred is set
+    bench = _bench()
+    inp = workloads.chunk_copy_inputs(5000, seed=9, sizes=tuple(range(0, 20)))
+    want = 0
+    for p, s, g in zip(inp.pred.tolist(), inp.src_size.tolist(), inp.ignore_src.tolist()):
+        want += 3
+        if p:
+            want += 16 + (0 if g else min(s, 16))
+    assert bench.chunk_copy_algorithmic_bytes(inp.pred, inp.src_size, inp.ignore_src) == want
+
+
+def test_chunk_copy_bytes_per_chunk_near_expectation():
+    # E[bytes] = 3 + 0.9 * 0.99 * 8 + 0.9 * 16 = 24.528 for the workload's draws
+    bench = _bench()
+    inp = workloads.chunk_copy_inputs(1 << 20, seed=3)
+    per_chunk = bench.chunk_copy_algorithmic_bytes(inp.pred, inp.src_size, inp.ignore_src) / (1 << 20)
+    assert abs(per_chunk - 24.528) < 0.05
+
+
+def test_sweep_points_are_told_apart_by_order():
+    # consecutive points never launch the same kernel on the same grid, so the
+    # per-point counter summaries can split dispatches by order
+    bench = _bench()
+    pts = bench.sweep_points()
+    assert len(pts) == len(set(pts)) == 36
+    A, B = 0x7f0000000000, 0x7f4000000000
+    keys = []
+    for off, align, tile, stages in pts:
+        p = tp.plan_map(A + 4 * off, B, 1 << 28, "scale2", tile, stages, 0, align=align)
+        keys.append((stages, p.lane_chunks, p.path, p.grid, p.threads))
+    assert all(a != b for a, b in zip(keys, keys[1:]))
+
+
+def test_stored_traffic_is_tied_to_the_sources():
+    bench = _bench()
+    h = bench.kernel_source_hash()
+    assert len(h) == 16 and int(h, 16) >= 0
+    entry = bench.stored_traffic("map_scale2_n268435456_t256_s2_T2")
+    # either the stored counters describe the current sources, or nothing is reported
+    assert entry is None or 2 * (1 << 30) <= entry < 2 * (1 << 30) * 1.01
