@@ -53,6 +53,11 @@ def parse():
                          "map with its default box (for counter passes); align: scale2 bandwidth "
                          "against the offsets of in and out from a 128-byte line, both policies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU work: read the rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE outputs "
+                         "of two runs of `bench.py --quick --no-cpu-baseline` (defaults otherwise), "
+                         "scale each counter by what it reads for the runtime's 1 GiB copy, and "
+                         "store the step's HBM bytes per launch in profiles/traffic.json")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline")
     return ap.parse_args()
@@ -142,8 +147,76 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(key: str):
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def step_traffic_key(n: int, tile: int, stages: int, tiles_per_block: int) -> str:
+    return f"map_scale2_n{n}_t{tile}_s{stages}_T{tiles_per_block}"
+
+
+def _counter_rows(directory: str, counter: str):
+    """(kernel name, grid size, value) of every dispatch in the rocprofv3
+    counter-collection CSVs under `directory`."""
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") == counter:
+                    rows.append((r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"])))
+    if not rows:
+        raise SystemExit(f"no {counter} rows under {directory}")
+    return rows
+
+
+def record_traffic(fetch_dir: str, write_dir: str, path: str | None = None):
+    """HBM bytes per launch of the step's map kernel from two counter runs.
+    Each counter is calibrated on the runtime's device-to-device copy of
+    1 GiB that the bench also runs (it reads and writes exactly 2^30 bytes):
+    scale = 2^30 / 1 KiB / counter KiB of that copy. The copy's dispatches are
+    the copyBuffer ones with the largest grid; the map kernel's value is the
+    median over its dispatches."""
+    gib_kib = float(1 << 20)
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(d, counter)
+        copies = [r for r in rows if "copyBuffer" in r[0]]
+        if not copies:
+            raise SystemExit(f"no runtime copy dispatch in {d}")
+        big = max(g for _, g, _ in copies)
+        copy_kib = median([v for _, g, v in copies if g == big])
+        maps = [v for k, _, v in rows if "map_kernel<0, 2, 1, true, true>" in k]
+        if not maps:
+            raise SystemExit(f"no map_kernel<scale2, S=2, L=1, x4, x4> dispatch in {d}")
+        out[counter] = {"scale": gib_kib / copy_kib, "map_kib": median(maps), "copy_kib": copy_kib,
+                        "dispatches": len(maps)}
+    fetch = out["FETCH_SIZE"]["map_kib"] * out["FETCH_SIZE"]["scale"] * 1024
+    write = out["WRITE_SIZE"]["map_kib"] * out["WRITE_SIZE"]["scale"] * 1024
+    n, tile, stages = 1 << 28, 256, 2
+    import software_pipelining_amd as tp
+    plan = tp.plan_map(1 << 40, 1 << 41, n, "scale2", tile, stages, 0)   # host-only planning
+    key = step_traffic_key(n, tile, stages, plan.tiles_per_block)
+    path = path or os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        table = {}
+    table[key] = {"kernel_source_hash": kernel_source_hash(),
+                  "bytes_per_launch": int(round(fetch + write)),
+                  "fetch_bytes": int(round(fetch)), "write_bytes": int(round(write)),
+                  "scale": {c: round(v["scale"], 5) for c, v in out.items()},
+                  "counter_kib": {c: {"map": v["map_kib"], "copy_1GiB": v["copy_kib"],
+                                      "map_dispatches": v["dispatches"]} for c, v in out.items()},
+                  "source": "profiles/map_scale2_2p28_t256_s2_T2_hbm_traffic.md"}
+    with open(path, "w") as f:
+        json.dump(table, f, indent=1)
+        f.write("\n")
+    alg = 8 * n
+    log(f"traffic {key}: fetch {fetch:.0f} B, write {write:.0f} B, "
+        f"{(fetch + write) / alg:.6f} x the algorithmic {alg} B")
+
+
+def stored_traffic(key: str, path: str | None = None):
+    path = path or os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
             d = json.load(f)
@@ -389,6 +462,9 @@ def align_mode(args):
 
 def main():
     args = parse()
+    if args.record_traffic:
+        record_traffic(*args.record_traffic)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the hot path needs no cross-GPU step and this "
               "build runs on a single MI355X; use --gpus 1", file=sys.stderr)
@@ -473,7 +549,7 @@ def main():
         "parity": "bit-exact on sampled windows" if parity else "MISMATCH",
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": stored_traffic(f"map_scale2_n{n}_t{T}_s{S}_T{plan.tiles_per_block}"),
+                     "traffic": stored_traffic(step_traffic_key(n, T, S, plan.tiles_per_block)),
                      "kernel": "map_kernel<scale2>", "algorithmic_bytes_per_launch": alg_bytes,
                      "avg_launch_us": round(avg_launch * 1e3, 2)},
     }

@@ -105,7 +105,10 @@ __device__ __forceinline__ u32x4 sgpr_res(const BufferRes &r)
 
 // ------------------------------------------------------- async copies to LDS
 // Lane l's bytes land at LDS address m0 + l * width (m0 wave-uniform).
-// `voff` is the lane's byte offset inside the resource.
+// `voff` is the lane's byte offset inside the resource. M0 is written without
+// being declared: the compiler reserves it and rejects it as a clobber. The
+// built kernels use M0 nowhere else (tests/test_isa_hazards.py checks that
+// every mention of M0 is one of these writes, followed by its load).
 __device__ __forceinline__ void dma_b128(const BufferRes &r, uint32_t voff, uint32_t m0)
 {
     asm volatile("s_mov_b32 m0, %2\n\t"

@@ -68,3 +68,41 @@ def test_stored_traffic_is_tied_to_the_sources():
     entry = bench.stored_traffic("map_scale2_n268435456_t256_s2_T2")
     # either the stored counters describe the current sources, or nothing is reported
     assert entry is None or 2 * (1 << 30) <= entry < 2 * (1 << 30) * 1.01
+
+
+def _counter_csv(path, counter, map_kib, copy_kib):
+    import csv
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    cols = ["Dispatch_Id", "Grid_Size", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(cols)
+        for i in range(3):
+            w.writerow([i, 1 << 25, "void tp::dev::map_kernel<0, 2, 1, true, true>(tp::MapParams)",
+                        counter, map_kib])
+        w.writerow([7, 1 << 25, "void tp::dev::map_kernel<1, 2, 1, true, true>(tp::MapParams)",
+                    counter, 1.0])
+        w.writerow([8, 1 << 25, "__amd_rocclr_copyBuffer", counter, copy_kib])   # the 1 GiB copy
+        w.writerow([9, 4096, "__amd_rocclr_copyBuffer", counter, 5.0])          # a staging copy
+
+
+def test_record_traffic_scales_by_the_copy(tmp_path):
+    # FETCH_SIZE reads half of a known 1 GiB copy, WRITE_SIZE all of it: the
+    # map's readings are scaled by 2 and 1, and the entry carries the hash of
+    # the sources it describes
+    bench = _bench()
+    _counter_csv(str(tmp_path / "f" / "h" / "1" / "x_counter_collection.csv"), "FETCH_SIZE",
+                 524300.0, 524288.0)
+    _counter_csv(str(tmp_path / "w" / "h" / "1" / "x_counter_collection.csv"), "WRITE_SIZE",
+                 1048576.0, 1048576.0)
+    out = str(tmp_path / "traffic.json")
+    bench.record_traffic(str(tmp_path / "f"), str(tmp_path / "w"), out)
+    plan = tp.plan_map(1 << 40, 1 << 41, 1 << 28, "scale2", 256, 2, 0)
+    key = bench.step_traffic_key(1 << 28, 256, 2, plan.tiles_per_block)
+    got = bench.stored_traffic(key, out)
+    assert got == 2 * 524300 * 1024 + 1048576 * 1024
+    import json
+    with open(out) as f:
+        e = json.load(f)[key]
+    assert e["scale"] == {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
+    assert e["kernel_source_hash"] == bench.kernel_source_hash()

@@ -117,6 +117,25 @@ def test_lds_dma_sets_m0_in_block(kernels):
                 assert insts[i - 2][0] == "s_mov_b32" and insts[i - 2][1][0] == "m0", (name, i)
 
 
+def test_m0_belongs_to_the_lds_dma_blocks(kernels):
+    # The asm blocks write M0 without declaring it (the compiler reserves that
+    # register and refuses it in a clobber list). That is only sound while no
+    # compiler-generated instruction keeps a value of its own in M0: every
+    # mention of M0 must be one of those writes, directly followed by the
+    # block's wait states and its LDS-DMA load.
+    n = 0
+    for name, insts in kernels.items():
+        for i, (op, ops) in enumerate(insts):
+            if not any(re.search(r"\bm0\b", t) for t in ops):
+                continue
+            assert op == "s_mov_b32" and ops[0] == "m0", (name, i, op, ops)
+            assert insts[i + 1][0] == "s_nop", (name, i)
+            nxt_op, nxt_ops = insts[i + 2]
+            assert nxt_op.startswith("buffer_load") and "lds" in nxt_ops[-1], (name, i, nxt_op)
+            n += 1
+    assert n > 1000
+
+
 def _vregs(tok: str):
     m = re.match(r"v\[(\d+):(\d+)\]", tok)
     if m:
