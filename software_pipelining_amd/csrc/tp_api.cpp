@@ -242,15 +242,7 @@ TP_API int tp_pipelined_map_ex(const float *in, float *out, int64_t n, int op, i
                       resident_cap, schedule, align, lds, &plan);
     if (st != TP_OK)
         return st;
-    tp::MapParams p;
-    memset(&p, 0, sizeof p);
-    p.in = in + plan.head;        // the tiled body
-    p.out = out + plan.head;
-    p.n = n - plan.head;
-    p.n_main = p.n & ~int64_t(3);
-    p.head = plan.head;
-    p.tiles_per_block = plan.tiles_per_block;
-    tp::horner32_coefficients(p.coef);
+    const tp::MapParams p = tp::map_params(plan, in, out, n);
     return finish_launch(launch_map(plan, p, op, stream));
 }
 
@@ -275,23 +267,8 @@ TP_API int tp_map_2d(const float *src, int64_t src_stride, float *dst, int64_t d
                          box_rows, box_cols, stages, boxes_per_block, align, lds, &plan);
     if (st != TP_OK)
         return st;
-    tp::Map2dParams p;
-    memset(&p, 0, sizeof p);
-    p.src = src;
-    p.dst = dst;
-    p.src_stride = src_stride;
-    p.dst_stride = dst_stride;
-    p.rows = rows;
-    p.cols = cols;
-    tp::map2d_resolve_box(cols, &box_rows, &box_cols);
-    int lg = 0;
-    while ((1 << lg) < box_cols)
-        ++lg;
-    p.box_cols_log2 = lg;
-    p.tiles_per_block = plan.tiles_per_block;
-    p.runs_per_band = (int32_t)((((cols + box_cols - 1) / box_cols) + plan.tiles_per_block - 1) /
-                                plan.tiles_per_block);
-    tp::horner32_coefficients(p.coef);
+    const tp::Map2dParams p = tp::map2d_params(plan, src, src_stride, dst, dst_stride, rows, cols,
+                                               box_rows, box_cols);
     return finish_launch(launch_map2d(plan, p, op, stream));
 }
 
@@ -323,17 +300,7 @@ TP_API int tp_chunk_copy_ex(const void *src, void *dst, int64_t n_chunks, int ch
         return st;
     if (plan.lds_bytes > lds)
         return TP_ERR_LDS_BUDGET;
-    tp::ChunkParams p;
-    memset(&p, 0, sizeof p);
-    p.src = static_cast<const uint8_t *>(src);
-    p.dst = static_cast<uint8_t *>(dst);
-    p.pred = pred;
-    p.src_size = src_size;
-    p.ignore_src = ignore_src;
-    p.n_chunks = n_chunks;
-    p.tiles_per_block = plan.tiles_per_block;
-    p.flags = (pred ? tp::kHasPred : 0) | (src_size ? tp::kHasSize : 0) |
-              (ignore_src ? tp::kHasIgnore : 0);
+    const tp::ChunkParams p = tp::chunk_params(plan, src, dst, n_chunks, pred, src_size, ignore_src);
     return finish_launch(tp::launch_chunk_copy(plan, p, stream));
 }
 

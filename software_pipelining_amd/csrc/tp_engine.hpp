@@ -177,9 +177,71 @@ __device__ __forceinline__ void block_sync()
     asm volatile("s_barrier" : : : "memory");
 }
 
+// ------------------------------------------------------------- the engine
+// What a kernel body is written against: the workgroup's indices, its LDS,
+// and the primitives above. Each kernel here is a thin __global__ wrapper
+// that instantiates its body (a template on the engine type) with this
+// engine. The same bodies compile on the host against the CPU emulator in
+// tests/emu, which runs every wave in lock-step and checks each access
+// against the caller's buffers, each LDS read against the waits that must
+// have retired its load, and LDS shared between waves against the barriers.
+struct GpuEngine {
+    uint8_t *lds;        // the workgroup's dynamic LDS
+    uint32_t nthreads_;  // blockDim.x, read in the kernel itself (see gpu_engine)
+
+    __device__ __forceinline__ uint32_t tid() const { return threadIdx.x; }
+    __device__ __forceinline__ uint32_t nthreads() const { return nthreads_; }
+    __device__ __forceinline__ uint32_t block() const { return blockIdx.x; }
+    __device__ __forceinline__ uint32_t blocks() const { return gridDim.x; }
+    __device__ __forceinline__ uint32_t uniform(uint32_t v) const { return dev::uniform(v); }
+    // LDS address of lds[0], as M0 takes it
+    __device__ __forceinline__ uint32_t lds_base() const { return lds_offset(lds); }
+    template <class T>
+    __device__ __forceinline__ T lds_load(uint32_t off) const
+    {
+        return *reinterpret_cast<const T *>(lds + off);
+    }
+    __device__ __forceinline__ BufferRes res(const void *base, uint32_t num_records) const
+    {
+        return make_buffer_res(base, num_records);
+    }
+    __device__ __forceinline__ void dma_b128(const BufferRes &r, uint32_t voff, uint32_t m0) const
+    {
+        dev::dma_b128(r, voff, m0);
+    }
+    __device__ __forceinline__ void dma_b32(const BufferRes &r, uint32_t voff, uint32_t m0) const
+    {
+        dev::dma_b32(r, voff, m0);
+    }
+    __device__ __forceinline__ void dma_u8(const BufferRes &r, uint32_t voff, uint32_t m0) const
+    {
+        dev::dma_u8(r, voff, m0);
+    }
+    __device__ __forceinline__ void store_b128(const BufferRes &r, uint32_t voff, u32x4 v) const
+    {
+        dev::store_b128(r, voff, v);
+    }
+    __device__ __forceinline__ void store_b32(const BufferRes &r, uint32_t voff, uint32_t v) const
+    {
+        dev::store_b32(r, voff, v);
+    }
+    template <int K>
+    __device__ __forceinline__ void wait() const
+    {
+        vm_wait<K>();
+    }
+    __device__ __forceinline__ void barrier() const { block_sync(); }
+};
+
+// The engine of a kernel whose dynamic LDS is `lds`. blockDim.x is read here,
+// in the kernel's own body: read inside the inlined kernel body instead, the
+// compiler no longer folds it to the launch's uniform group size and loads
+// the group size from the implicit arguments with a vector load.
+#define TP_GPU_ENGINE(lds) (::tp::dev::GpuEngine{(lds), blockDim.x})
+
 // ---------------------------------------------------------------- helpers
 template <int Begin, int End, typename F>
-__device__ __forceinline__ void static_for(F &&f)
+__host__ __device__ __forceinline__ void static_for(F &&f)
 {
     if constexpr (Begin < End) {
         f(std::integral_constant<int, Begin>{});

@@ -164,6 +164,24 @@ struct ChunkParams {
     int32_t flags;           // ChunkFlags
 };
 
+// Kernel arguments of a planned chunk copy (an absent metadata array is a
+// null pointer and a cleared flag).
+inline ChunkParams chunk_params(const tp_plan &plan, const void *src, void *dst, int64_t n_chunks,
+                                const uint8_t *pred, const uint8_t *src_size,
+                                const uint8_t *ignore_src)
+{
+    ChunkParams p{};
+    p.src = static_cast<const uint8_t *>(src);
+    p.dst = static_cast<uint8_t *>(dst);
+    p.pred = pred;
+    p.src_size = src_size;
+    p.ignore_src = ignore_src;
+    p.n_chunks = n_chunks;
+    p.tiles_per_block = plan.tiles_per_block;
+    p.flags = (pred ? kHasPred : 0) | (src_size ? kHasSize : 0) | (ignore_src ? kHasIgnore : 0);
+    return p;
+}
+
 // -------------------------------------------------------------- row shift
 struct RowShiftParams {
     const float *a;
@@ -193,6 +211,11 @@ int plan_chunk_copy(uintptr_t src, uintptr_t dst, int64_t n_chunks, int chunk_by
 
 // Horner coefficients c_k = RN(1/(k+1)), k = 0..31.
 void horner32_coefficients(float c[32]);
+
+// Kernel arguments of a planned launch, as the C ABI builds them.
+MapParams map_params(const tp_plan &plan, const float *in, float *out, int64_t n);
+Map2dParams map2d_params(const tp_plan &plan, const float *src, int64_t src_stride, float *dst,
+                         int64_t dst_stride, int64_t rows, int64_t cols, int box_rows, int box_cols);
 
 // ------------------------------------------------------- kernel launchers
 // Each returns a hipError_t value (0 = success). `stream` is a hipStream_t.

@@ -31,7 +31,7 @@ struct MapOp;
 template <>
 struct MapOp<TP_OP_SCALE2> {
     template <int N>
-    __device__ __forceinline__ static void apply(float (&v)[N], const float *)
+    TP_HD __forceinline__ static void apply(float (&v)[N], const float *)
     {
 #pragma unroll
         for (int i = 0; i < N; ++i)
@@ -42,7 +42,7 @@ struct MapOp<TP_OP_SCALE2> {
 template <>
 struct MapOp<TP_OP_COPY> {
     template <int N>
-    __device__ __forceinline__ static void apply(float (&)[N], const float *) {}
+    TP_HD __forceinline__ static void apply(float (&)[N], const float *) {}
 };
 
 // y = 0; y = fma(y, x, c_k) for k = 0..31. The N elements of a lane form N
@@ -51,7 +51,7 @@ struct MapOp<TP_OP_COPY> {
 template <>
 struct MapOp<TP_OP_HORNER32> {
     template <int N>
-    __device__ __forceinline__ static void apply(float (&v)[N], const float *c)
+    TP_HD __forceinline__ static void apply(float (&v)[N], const float *c)
     {
         float y[N];
 #pragma unroll
@@ -70,61 +70,62 @@ struct MapOp<TP_OP_HORNER32> {
     }
 };
 
-__device__ __forceinline__ uint32_t f2u(float x) { return __builtin_bit_cast(uint32_t, x); }
+TP_HD __forceinline__ uint32_t f2u(float x) { return __builtin_bit_cast(uint32_t, x); }
 
 // `count` (at most 64) floats outside the body's whole 16-byte chunks, moved
 // element-wise by one wave: lane l loads src[l] into the LDS area at byte
-// address `area` (lanes past `count` are out of range: they move nothing and
-// store nothing), waits for its own copy, applies the op and stores dst[l].
-template <int OP>
-__device__ __forceinline__ void map_edge(const float *src, float *dst, uint32_t count, uint32_t area,
-                                         const uint8_t *area_ptr, uint32_t lane, const float *coef)
+// offset `area_off` of the workgroup's LDS (lanes past `count` are out of
+// range: they move nothing and store nothing), waits for its own copy, applies
+// the op and stores dst[l].
+template <int OP, class E>
+TP_HD __forceinline__ void map_edge(const E &e, const float *src, float *dst, uint32_t count,
+                                    uint32_t area_off, uint32_t lane, const float *coef)
 {
-    const BufferRes ri = make_buffer_res(src, count * 4);
-    const BufferRes ro = make_buffer_res(dst, count * 4);
-    dma_b32(ri, lane * 4, uniform(area));
-    vm_wait<0>();
-    float v[1] = {*reinterpret_cast<const float *>(area_ptr + lane * 4)};
+    const auto ri = e.res(src, count * 4);
+    const auto ro = e.res(dst, count * 4);
+    e.dma_b32(ri, lane * 4, e.uniform(e.lds_base() + area_off));
+    e.template wait<0>();
+    float v[1] = {e.template lds_load<float>(area_off + lane * 4)};
     MapOp<OP>::apply(v, coef);
-    store_b32(ro, lane * 4, f2u(v[0]));
+    e.store_b32(ro, lane * 4, f2u(v[0]));
 }
 
-template <int OP, int S, int L, bool LX4, bool SX4>
-__global__ void __launch_bounds__(256) map_kernel(MapParams p)
+// The kernel body, written against an engine (tp_engine.hpp).
+template <class E, int OP, int S, int L, bool LX4, bool SX4>
+TP_HD __forceinline__ void map_body(const E &e, const MapParams &p)
 {
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     constexpr int LD = map_loads_per_tile(LX4, L);
     constexpr int ST = map_stores_per_tile(SX4, L);
 
-    const uint32_t nt = blockDim.x;
-    const uint32_t tid = threadIdx.x;
-    const uint32_t wave_first = uniform(tid & ~63u);
+    const uint32_t nt = e.nthreads();
+    const uint32_t tid = e.tid();
+    const uint32_t wave_first = e.uniform(tid & ~63u);
     const uint32_t tile_bytes = nt * L * 16;
     const int64_t tile_elems = (int64_t)nt * L * 4;
 
     // This workgroup's run: tiles [b T, (b + 1) T) of the input, tile j at
     // byte j * tile_bytes of the resource window [base, base + span).
-    const uint32_t b = blockIdx.x;
+    const uint32_t b = e.block();
     const int64_t run_first = (int64_t)b * p.tiles_per_block * tile_elems;
     const int64_t rem = p.n_main - run_first;
     const int64_t run_bytes = (int64_t)p.tiles_per_block * tile_bytes;
     const uint32_t span = rem <= 0 ? 0u : (uint32_t)(rem * 4 < run_bytes ? rem * 4 : run_bytes);
     const int64_t base = rem > 0 ? run_first : 0;
     const int cnt = (int)((span + tile_bytes - 1) / tile_bytes);
-    const BufferRes rin = make_buffer_res(p.in + base, span);
-    const BufferRes rout = make_buffer_res(p.out + base, span);
-    const uint32_t ring = uniform(lds_offset(lds));
+    const auto rin = e.res(p.in + base, span);
+    const auto rout = e.res(p.out + base, span);
+    const uint32_t ring = e.uniform(e.lds_base());
 
     // Producer: copy tile j of the run into the LDS slot at byte address `slot`.
     auto issue = [&](uint32_t j, uint32_t slot) TP_INLINE {
         const uint32_t toff = j * tile_bytes;
         if constexpr (LX4) {
             static_for<0, L>([&](auto i) TP_INLINE {
-                dma_b128(rin, toff + (i * nt + tid) * 16, uniform(slot + (i * nt + wave_first) * 16));
+                e.dma_b128(rin, toff + (i * nt + tid) * 16, e.uniform(slot + (i * nt + wave_first) * 16));
             });
         } else {
             static_for<0, 4 * L>([&](auto i) TP_INLINE {
-                dma_b32(rin, toff + (i * nt + tid) * 4, uniform(slot + (i * nt + wave_first) * 4));
+                e.dma_b32(rin, toff + (i * nt + tid) * 4, e.uniform(slot + (i * nt + wave_first) * 4));
             });
         }
     };
@@ -135,7 +136,7 @@ __global__ void __launch_bounds__(256) map_kernel(MapParams p)
         float v[4 * L];
         if constexpr (SX4) {
             static_for<0, L>([&](auto i) TP_INLINE {
-                const f32x4 x = *reinterpret_cast<const f32x4 *>(lds + slot_off + (i * nt + tid) * 16);
+                const f32x4 x = e.template lds_load<f32x4>(slot_off + (i * nt + tid) * 16);
                 v[4 * i + 0] = x.x;
                 v[4 * i + 1] = x.y;
                 v[4 * i + 2] = x.z;
@@ -144,19 +145,19 @@ __global__ void __launch_bounds__(256) map_kernel(MapParams p)
             MapOp<OP>::apply(v, p.coef);
             static_for<0, L>([&](auto i) TP_INLINE {
                 const u32x4 o = {f2u(v[4 * i]), f2u(v[4 * i + 1]), f2u(v[4 * i + 2]), f2u(v[4 * i + 3])};
-                store_b128(rout, toff + (i * nt + tid) * 16, o);
+                e.store_b128(rout, toff + (i * nt + tid) * 16, o);
             });
         } else {
             static_for<0, 4 * L>([&](auto i) TP_INLINE {
-                v[i] = *reinterpret_cast<const float *>(lds + slot_off + (i * nt + tid) * 4);
+                v[i] = e.template lds_load<float>(slot_off + (i * nt + tid) * 4);
             });
             MapOp<OP>::apply(v, p.coef);
-            static_for<0, 4 * L>([&](auto i) TP_INLINE { store_b32(rout, toff + (i * nt + tid) * 4, f2u(v[i])); });
+            static_for<0, 4 * L>([&](auto i) TP_INLINE { e.store_b32(rout, toff + (i * nt + tid) * 4, f2u(v[i])); });
         }
     };
 
     if (cnt > 0)
-        pipeline_run<S, LD, ST, map_wave_local(LX4, SX4)>(cnt, ring, tile_bytes, issue, consume);
+        pipeline_run<S, LD, ST, map_wave_local(LX4, SX4)>(e, cnt, ring, tile_bytes, issue, consume);
 
     // The floats outside the body's whole 16-byte chunks, moved element-wise
     // by the first wave through an LDS area of its own: the 0-31 floats before
@@ -165,14 +166,20 @@ __global__ void __launch_bounds__(256) map_kernel(MapParams p)
     if (wave_first == 0) {
         const uint32_t edge_off = S * tile_bytes;
         if (b == 0 && p.head > 0)
-            map_edge<OP>(p.in - p.head, p.out - p.head, (uint32_t)p.head, ring + edge_off,
-                         lds + edge_off, tid, p.coef);
-        if (b == gridDim.x - 1 && p.n > p.n_main)
-            map_edge<OP>(p.in + p.n_main, p.out + p.n_main, (uint32_t)(p.n - p.n_main),
-                         ring + edge_off, lds + edge_off, tid, p.coef);
+            map_edge<OP>(e, p.in - p.head, p.out - p.head, (uint32_t)p.head, edge_off, tid, p.coef);
+        if (b == e.blocks() - 1 && p.n > p.n_main)
+            map_edge<OP>(e, p.in + p.n_main, p.out + p.n_main, (uint32_t)(p.n - p.n_main), edge_off,
+                         tid, p.coef);
     }
     // No copy into LDS is in flight here: pipeline_run retires its last load
     // before it returns, and each edge pass waits for its own.
+}
+
+template <int OP, int S, int L, bool LX4, bool SX4>
+__global__ void __launch_bounds__(256) map_kernel(MapParams p)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    map_body<GpuEngine, OP, S, L, LX4, SX4>(TP_GPU_ENGINE(lds), p);
 }
 
 // Kernel table of one op over stage counts SLO..SHI:

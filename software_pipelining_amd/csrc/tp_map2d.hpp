@@ -28,23 +28,23 @@
 namespace tp {
 namespace dev {
 
-template <int OP, int S, int L, bool LX4, bool SX4>
-__global__ void __launch_bounds__(256) map2d_kernel(Map2dParams p)
+// The kernel body, written against an engine (tp_engine.hpp).
+template <class E, int OP, int S, int L, bool LX4, bool SX4>
+TP_HD __forceinline__ void map2d_body(const E &e, const Map2dParams &p)
 {
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     constexpr int LD = map_loads_per_tile(LX4, L);
     constexpr int ST = map_stores_per_tile(SX4, L);
 
-    const uint32_t nt = blockDim.x;
-    const uint32_t tid = threadIdx.x;
-    const uint32_t wave_first = uniform(tid & ~63u);
+    const uint32_t nt = e.nthreads();
+    const uint32_t tid = e.tid();
+    const uint32_t wave_first = e.uniform(tid & ~63u);
     const uint32_t tile_bytes = nt * L * 16;
     const uint32_t bc_log2 = p.box_cols_log2;
     const uint32_t box_cols = 1u << bc_log2;
     const uint32_t box_rows = (nt * L * 4) >> bc_log2;
 
     // This workgroup's run: boxes [first_box, first_box + T) of band `band`.
-    const uint32_t b = blockIdx.x;
+    const uint32_t b = e.block();
     const uint32_t band = b / p.runs_per_band;
     const uint32_t first_box = (b - band * p.runs_per_band) * p.tiles_per_block;
     const int64_t r0 = (int64_t)band * box_rows;
@@ -59,9 +59,9 @@ __global__ void __launch_bounds__(256) map2d_kernel(Map2dParams p)
     const uint32_t ds = (uint32_t)p.dst_stride;
     const uint32_t src_end = ((rr - 1) * ss + cc) * 4;   // first out-of-range byte
     const uint32_t dst_end = ((rr - 1) * ds + cc) * 4;
-    const BufferRes rin = make_buffer_res(p.src + r0 * p.src_stride + c0, src_end);
-    const BufferRes rout = make_buffer_res(p.dst + r0 * p.dst_stride + c0, dst_end);
-    const uint32_t ring = uniform(lds_offset(lds));
+    const auto rin = e.res(p.src + r0 * p.src_stride + c0, src_end);
+    const auto rout = e.res(p.dst + r0 * p.dst_stride + c0, dst_end);
+    const uint32_t ring = e.uniform(e.lds_base());
 
     // Element e of box j (row-major in the box, 4-aligned on the 16-byte
     // path): its byte offset in a descriptor with row stride `stride`, or
@@ -76,12 +76,12 @@ __global__ void __launch_bounds__(256) map2d_kernel(Map2dParams p)
         if constexpr (LX4) {
             static_for<0, L>([&](auto i) TP_INLINE {
                 const uint32_t q = i * nt + tid;   // 16-byte chunk of the box
-                dma_b128(rin, elem_offset(j, q * 4, ss, src_end), uniform(slot + (i * nt + wave_first) * 16));
+                e.dma_b128(rin, elem_offset(j, q * 4, ss, src_end), e.uniform(slot + (i * nt + wave_first) * 16));
             });
         } else {
             static_for<0, 4 * L>([&](auto i) TP_INLINE {
                 const uint32_t f = i * nt + tid;   // float of the box
-                dma_b32(rin, elem_offset(j, f, ss, src_end), uniform(slot + (i * nt + wave_first) * 4));
+                e.dma_b32(rin, elem_offset(j, f, ss, src_end), e.uniform(slot + (i * nt + wave_first) * 4));
             });
         }
     };
@@ -90,7 +90,7 @@ __global__ void __launch_bounds__(256) map2d_kernel(Map2dParams p)
         float v[4 * L];
         if constexpr (SX4) {
             static_for<0, L>([&](auto i) TP_INLINE {
-                const f32x4 x = *reinterpret_cast<const f32x4 *>(lds + slot_off + (i * nt + tid) * 16);
+                const f32x4 x = e.template lds_load<f32x4>(slot_off + (i * nt + tid) * 16);
                 v[4 * i + 0] = x.x;
                 v[4 * i + 1] = x.y;
                 v[4 * i + 2] = x.z;
@@ -99,20 +99,27 @@ __global__ void __launch_bounds__(256) map2d_kernel(Map2dParams p)
             MapOp<OP>::apply(v, p.coef);
             static_for<0, L>([&](auto i) TP_INLINE {
                 const u32x4 o = {f2u(v[4 * i]), f2u(v[4 * i + 1]), f2u(v[4 * i + 2]), f2u(v[4 * i + 3])};
-                store_b128(rout, elem_offset(j, (i * nt + tid) * 4, ds, dst_end), o);
+                e.store_b128(rout, elem_offset(j, (i * nt + tid) * 4, ds, dst_end), o);
             });
         } else {
             static_for<0, 4 * L>([&](auto i) TP_INLINE {
-                v[i] = *reinterpret_cast<const float *>(lds + slot_off + (i * nt + tid) * 4);
+                v[i] = e.template lds_load<float>(slot_off + (i * nt + tid) * 4);
             });
             MapOp<OP>::apply(v, p.coef);
             static_for<0, 4 * L>([&](auto i) TP_INLINE {
-                store_b32(rout, elem_offset(j, i * nt + tid, ds, dst_end), f2u(v[i]));
+                e.store_b32(rout, elem_offset(j, i * nt + tid, ds, dst_end), f2u(v[i]));
             });
         }
     };
 
-    pipeline_run<S, LD, ST, map_wave_local(LX4, SX4)>(cnt, ring, tile_bytes, issue, consume);
+    pipeline_run<S, LD, ST, map_wave_local(LX4, SX4)>(e, cnt, ring, tile_bytes, issue, consume);
+}
+
+template <int OP, int S, int L, bool LX4, bool SX4>
+__global__ void __launch_bounds__(256) map2d_kernel(Map2dParams p)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    map2d_body<GpuEngine, OP, S, L, LX4, SX4>(TP_GPU_ENGINE(lds), p);
 }
 
 // Kernel table of one op over stage counts SLO..SHI:

@@ -45,10 +45,10 @@ struct SplitGeometry {
     static constexpr int L = TILE / (4 * NC);                   // 16-byte chunks per consumer lane
 };
 
-template <int OP, int S, int TILE, bool LX4, bool SX4>
-__global__ void __launch_bounds__(320) map_split_kernel(MapParams p)
+// The kernel body, written against an engine (tp_engine.hpp).
+template <class E, int OP, int S, int TILE, bool LX4, bool SX4>
+TP_HD __forceinline__ void map_split_body(const E &e, const MapParams &p)
 {
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     using G = SplitGeometry<TILE>;
     constexpr int NC = G::NC;
     constexpr int L = G::L;
@@ -56,21 +56,21 @@ __global__ void __launch_bounds__(320) map_split_kernel(MapParams p)
     constexpr uint32_t tile_bytes = TILE * 4;
     constexpr int64_t tile_elems = TILE;
 
-    const uint32_t tid = threadIdx.x;
-    const uint32_t wave_first = uniform(tid & ~63u);
+    const uint32_t tid = e.tid();
+    const uint32_t wave_first = e.uniform(tid & ~63u);
     const bool producer = wave_first >= (uint32_t)NC;
 
     // This workgroup's run: tiles [b T, (b + 1) T), as in the uniform schedule.
-    const uint32_t b = blockIdx.x;
+    const uint32_t b = e.block();
     const int64_t run_first = (int64_t)b * p.tiles_per_block * tile_elems;
     const int64_t rem = p.n_main - run_first;
     const int64_t run_bytes = (int64_t)p.tiles_per_block * tile_bytes;
     const uint32_t span = rem <= 0 ? 0u : (uint32_t)(rem * 4 < run_bytes ? rem * 4 : run_bytes);
     const int64_t base = rem > 0 ? run_first : 0;
     const int cnt = (int)((span + tile_bytes - 1) / tile_bytes);
-    const BufferRes rin = make_buffer_res(p.in + base, span);
-    const BufferRes rout = make_buffer_res(p.out + base, span);
-    const uint32_t ring = uniform(lds_offset(lds));
+    const auto rin = e.res(p.in + base, span);
+    const auto rout = e.res(p.out + base, span);
+    const uint32_t ring = e.uniform(e.lds_base());
 
     // Producer: every chunk of tile j into the LDS slot at byte address `slot`.
     auto issue = [&](uint32_t j, uint32_t slot) TP_INLINE {
@@ -78,11 +78,11 @@ __global__ void __launch_bounds__(320) map_split_kernel(MapParams p)
         const uint32_t pl = tid - NC;
         if constexpr (LX4) {
             static_for<0, LDP>([&](auto k) TP_INLINE {
-                dma_b128(rin, toff + (k * 64 + pl) * 16, uniform(slot + k * 64 * 16));
+                e.dma_b128(rin, toff + (k * 64 + pl) * 16, e.uniform(slot + k * 64 * 16));
             });
         } else {
             static_for<0, LDP>([&](auto k) TP_INLINE {
-                dma_b32(rin, toff + (k * 64 + pl) * 4, uniform(slot + k * 64 * 4));
+                e.dma_b32(rin, toff + (k * 64 + pl) * 4, e.uniform(slot + k * 64 * 4));
             });
         }
     };
@@ -93,7 +93,7 @@ __global__ void __launch_bounds__(320) map_split_kernel(MapParams p)
         float v[4 * L];
         if constexpr (SX4) {
             static_for<0, L>([&](auto i) TP_INLINE {
-                const f32x4 x = *reinterpret_cast<const f32x4 *>(lds + slot_off + (i * NC + tid) * 16);
+                const f32x4 x = e.template lds_load<f32x4>(slot_off + (i * NC + tid) * 16);
                 v[4 * i + 0] = x.x;
                 v[4 * i + 1] = x.y;
                 v[4 * i + 2] = x.z;
@@ -102,14 +102,14 @@ __global__ void __launch_bounds__(320) map_split_kernel(MapParams p)
             MapOp<OP>::apply(v, p.coef);
             static_for<0, L>([&](auto i) TP_INLINE {
                 const u32x4 o = {f2u(v[4 * i]), f2u(v[4 * i + 1]), f2u(v[4 * i + 2]), f2u(v[4 * i + 3])};
-                store_b128(rout, toff + (i * NC + tid) * 16, o);
+                e.store_b128(rout, toff + (i * NC + tid) * 16, o);
             });
         } else {
             static_for<0, 4 * L>([&](auto i) TP_INLINE {
-                v[i] = *reinterpret_cast<const float *>(lds + slot_off + (i * NC + tid) * 4);
+                v[i] = e.template lds_load<float>(slot_off + (i * NC + tid) * 4);
             });
             MapOp<OP>::apply(v, p.coef);
-            static_for<0, 4 * L>([&](auto i) TP_INLINE { store_b32(rout, toff + (i * NC + tid) * 4, f2u(v[i])); });
+            static_for<0, 4 * L>([&](auto i) TP_INLINE { e.store_b32(rout, toff + (i * NC + tid) * 4, f2u(v[i])); });
         }
     };
 
@@ -118,28 +118,28 @@ __global__ void __launch_bounds__(320) map_split_kernel(MapParams p)
             if constexpr (S == 1) {
                 for (int t = 0; t < cnt; ++t) {
                     issue(t, ring);
-                    vm_wait<0>();
-                    block_sync();   // tile t is in LDS
-                    block_sync();   // the consumers are done with it
+                    e.template wait<0>();
+                    e.barrier();   // tile t is in LDS
+                    e.barrier();   // the consumers are done with it
                 }
             } else {
                 static_for<0, S - 1>([&](auto s) TP_INLINE { issue(s, ring + s * tile_bytes); });
                 uint32_t nxt = S - 1;  // slot of tile t + S - 1
                 for (int t = 0; t < cnt; ++t) {
-                    vm_wait<stage_wait_count(S, LDP, 0, 0)>();
-                    block_sync();
+                    e.template wait<stage_wait_count(S, LDP, 0, 0)>();
+                    e.barrier();
                     issue(t + S - 1, ring + nxt * tile_bytes);
                     nxt = nxt + 1 == S ? 0 : nxt + 1;
                 }
             }
-            vm_wait<0>();   // the loads issued past the run's end
+            e.template wait<0>();   // the loads issued past the run's end
         } else {
             uint32_t cur = 0;  // slot of tile t
             for (int t = 0; t < cnt; ++t) {
-                block_sync();
+                e.barrier();
                 consume(t, cur * tile_bytes);
                 if constexpr (S == 1)
-                    block_sync();
+                    e.barrier();
                 cur = cur + 1 == S ? 0 : cur + 1;
             }
         }
@@ -151,12 +151,18 @@ __global__ void __launch_bounds__(320) map_split_kernel(MapParams p)
     if (wave_first == 0) {
         const uint32_t edge_off = S * tile_bytes;
         if (b == 0 && p.head > 0)
-            map_edge<OP>(p.in - p.head, p.out - p.head, (uint32_t)p.head, ring + edge_off,
-                         lds + edge_off, tid, p.coef);
-        if (b == gridDim.x - 1 && p.n > p.n_main)
-            map_edge<OP>(p.in + p.n_main, p.out + p.n_main, (uint32_t)(p.n - p.n_main),
-                         ring + edge_off, lds + edge_off, tid, p.coef);
+            map_edge<OP>(e, p.in - p.head, p.out - p.head, (uint32_t)p.head, edge_off, tid, p.coef);
+        if (b == e.blocks() - 1 && p.n > p.n_main)
+            map_edge<OP>(e, p.in + p.n_main, p.out + p.n_main, (uint32_t)(p.n - p.n_main), edge_off,
+                         tid, p.coef);
     }
+}
+
+template <int OP, int S, int TILE, bool LX4, bool SX4>
+__global__ void __launch_bounds__(320) map_split_kernel(MapParams p)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    map_split_body<GpuEngine, OP, S, TILE, LX4, SX4>(TP_GPU_ENGINE(lds), p);
 }
 
 // Kernel table of one op over stage counts SLO..SHI:

@@ -34,7 +34,7 @@
 // immediate (the first S-1 iterations, whose loads were issued before any
 // store, are peeled with their own smaller counts).
 //
-// The caller supplies the tile: issue(j, slot_address) issues the LD loads of
+// The caller supplies the engine (tp_engine.hpp) and the tile: issue(j, slot_address) issues the LD loads of
 // tile j into the slot at that LDS byte address (out-of-range loads for j past
 // the run move nothing), and consume(j, slot_offset) reads tile j from the
 // slot at that byte offset of the workgroup's LDS, computes and issues its ST
@@ -50,9 +50,9 @@ namespace dev {
 
 // Runs the loop for cnt >= 1 tiles; on return no load issued here is still in
 // flight (only the last tiles' stores may be), so the LDS may be released.
-template <int S, int LD, int ST, bool WAVE_LOCAL, class Issue, class Consume>
-__device__ __forceinline__ void pipeline_run(int cnt, uint32_t ring, uint32_t slot_bytes,
-                                             Issue &issue, Consume &consume)
+template <int S, int LD, int ST, bool WAVE_LOCAL, class E, class Issue, class Consume>
+TP_HD __forceinline__ void pipeline_run(const E &e, int cnt, uint32_t ring, uint32_t slot_bytes,
+                                        Issue &issue, Consume &consume)
 {
     if constexpr (WAVE_LOCAL) {
         static_for<0, S - 1>([&](auto s) TP_INLINE { issue(s, ring + s * slot_bytes); });
@@ -63,7 +63,7 @@ __device__ __forceinline__ void pipeline_run(int cnt, uint32_t ring, uint32_t sl
         static_for<0, S - 1>([&](auto T) TP_INLINE {
             if ((int)T == 0 || (int)T < cnt) {
                 issue(T + S - 1, ring + ((T + S - 1) % S) * slot_bytes);
-                vm_wait<stage_wait_count(S, LD, ST, T, true)>();
+                e.template wait<stage_wait_count(S, LD, ST, T, true)>();
                 consume(T, (T % S) * slot_bytes);
             }
         });
@@ -71,24 +71,24 @@ __device__ __forceinline__ void pipeline_run(int cnt, uint32_t ring, uint32_t sl
         for (int t = S - 1; t < cnt; ++t) {
             const uint32_t nxt = cur == 0 ? S - 1 : cur - 1;  // slot of tile t + S - 1
             issue(t + S - 1, ring + nxt * slot_bytes);
-            vm_wait<stage_wait_count(S, LD, ST, S - 1, true)>();
+            e.template wait<stage_wait_count(S, LD, ST, S - 1, true)>();
             consume(t, cur * slot_bytes);
             cur = cur + 1 == S ? 0 : cur + 1;
         }
     } else if constexpr (S == 1) {
         for (int t = 0; t < cnt; ++t) {
             issue(t, ring);
-            vm_wait<0>();
-            block_sync();
+            e.template wait<0>();
+            e.barrier();
             consume(t, 0);
-            block_sync();
+            e.barrier();
         }
     } else {
         static_for<0, S - 1>([&](auto s) TP_INLINE { issue(s, ring + s * slot_bytes); });
         static_for<0, S - 1>([&](auto T) TP_INLINE {
             if ((int)T == 0 || (int)T < cnt) {    // cnt is uniform: every wave takes the barrier
-                vm_wait<stage_wait_count(S, LD, ST, T)>();
-                block_sync();
+                e.template wait<stage_wait_count(S, LD, ST, T)>();
+                e.barrier();
                 issue(T + S - 1, ring + ((T + S - 1) % S) * slot_bytes);
                 consume(T, (T % S) * slot_bytes);
             }
@@ -96,8 +96,8 @@ __device__ __forceinline__ void pipeline_run(int cnt, uint32_t ring, uint32_t sl
         uint32_t cur = (S - 1) % S;  // slot of tile t
         for (int t = S - 1; t < cnt; ++t) {
             const uint32_t nxt = cur == 0 ? S - 1 : cur - 1;  // slot of tile t + S - 1
-            vm_wait<stage_wait_count(S, LD, ST, S - 1)>();
-            block_sync();
+            e.template wait<stage_wait_count(S, LD, ST, S - 1)>();
+            e.barrier();
             issue(t + S - 1, ring + nxt * slot_bytes);
             consume(t, cur * slot_bytes);
             cur = cur + 1 == S ? 0 : cur + 1;
@@ -106,7 +106,7 @@ __device__ __forceinline__ void pipeline_run(int cnt, uint32_t ring, uint32_t sl
     // Operations retire in issue order and every path above ends with one
     // tile's ST stores issued after the last load, so at most ST outstanding
     // means every load has landed.
-    vm_wait<ST>();
+    e.template wait<ST>();
 }
 
 }  // namespace dev

@@ -359,4 +359,41 @@ void horner32_coefficients(float c[32])
         c[k] = 1.0f / (float)(k + 1);
 }
 
+MapParams map_params(const tp_plan &plan, const float *in, float *out, int64_t n)
+{
+    MapParams p;
+    memset(&p, 0, sizeof p);
+    p.in = in + plan.head;        // the tiled body
+    p.out = out + plan.head;
+    p.n = n - plan.head;
+    p.n_main = p.n & ~int64_t(3);
+    p.head = plan.head;
+    p.tiles_per_block = plan.tiles_per_block;
+    horner32_coefficients(p.coef);
+    return p;
+}
+
+Map2dParams map2d_params(const tp_plan &plan, const float *src, int64_t src_stride, float *dst,
+                         int64_t dst_stride, int64_t rows, int64_t cols, int box_rows, int box_cols)
+{
+    Map2dParams p;
+    memset(&p, 0, sizeof p);
+    p.src = src;
+    p.dst = dst;
+    p.src_stride = src_stride;
+    p.dst_stride = dst_stride;
+    p.rows = rows;
+    p.cols = cols;
+    map2d_resolve_box(cols, &box_rows, &box_cols);
+    int lg = 0;
+    while ((1 << lg) < box_cols)
+        ++lg;
+    p.box_cols_log2 = lg;
+    p.tiles_per_block = plan.tiles_per_block;
+    p.runs_per_band = (int32_t)((((cols + box_cols - 1) / box_cols) + plan.tiles_per_block - 1) /
+                                plan.tiles_per_block);
+    horner32_coefficients(p.coef);
+    return p;
+}
+
 }  // namespace tp
