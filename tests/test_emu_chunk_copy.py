@@ -198,3 +198,27 @@ def test_planted_short_source_is_reported():
     regions = [(src[:-16], False), (dst, True)] + [(m, False) for m in meta]
     with pytest.raises(emu.EmulationError, match="reads outside every buffer"):
         emu.chunk_copy(src, dst, *meta, stages=3, regions=regions)
+
+
+def test_random_configurations():
+    # sizes, stages, runs, chunk widths, offsets, metadata presence and value
+    # mixes drawn jointly
+    rng = np.random.default_rng(17)
+    for i in range(60):
+        width = int(rng.choice([16, 16, 8, 4]))
+        n = int(rng.choice([rng.integers(1, 300), rng.integers(1, 3000), rng.integers(1, 20000)]))
+        stages = int(rng.integers(1, 9))
+        tpb = int(rng.choice([0, 1, 2, 5, 64]))
+        src_off, dst_off = (int(rng.integers(0, 4)), int(rng.integers(0, 4)))
+        use = tuple(bool(rng.random() < 0.8) for _ in range(3))
+        src = _at(n * width, src_off, rng.integers(0, 256, n * width, dtype=np.uint8))
+        dst = _at(n * width, dst_off, rng.integers(0, 256, n * width, dtype=np.uint8))
+        meta = [rng.integers(0, 2, n, dtype=np.uint8) * rng.integers(1, 256, n, dtype=np.uint8),
+                rng.integers(0, width + 4, n, dtype=np.uint8),
+                (rng.random(n) < rng.choice([0.0, 0.05, 0.5])).astype(np.uint8)]
+        meta = [m if u else None for m, u in zip(meta, use)]
+        expected = oracle.chunk_copy(src, dst, *meta, chunk_bytes=width)
+        plan = emu.chunk_copy(src, dst, *meta, chunk_bytes=width, stages=stages,
+                              tiles_per_block=tpb, policy=i % 2, seed=i)
+        assert np.array_equal(dst, expected), (i, width, n, stages, tpb, src_off, dst_off, use,
+                                               plan.path)
