@@ -71,6 +71,9 @@ struct Options {
     int n_regions;
     const int64_t *blocks;   // workgroups to run (all when null)
     int n_blocks;
+    int oor_fill;        // what an out-of-range lane's load leaves in its LDS slot:
+                         // 0 zeros (measured on the MI355X), 1 random bytes (the
+                         // kernels must not depend on it)
 };
 
 struct Fail : std::runtime_error {
@@ -199,6 +202,7 @@ class Emulator {
     Options opt;
     uint32_t nthreads, lds_bytes, grid;
     std::mt19937_64 rng;
+    std::mt19937 oor_rng{12345};
     std::function<void()> body_;
     uint32_t block = 0;
     ucontext_t sched;
@@ -420,7 +424,11 @@ class Emulator {
         for (const Xfer &x : op.x) {
             uint8_t v[16] = {0};
             for (int i = 0; i < x.nbytes; ++i)
-                v[i] = x.addr[i] ? *reinterpret_cast<const uint8_t *>(x.addr[i]) : 0;
+                v[i] = x.addr[i] ? *reinterpret_cast<const uint8_t *>(x.addr[i])
+                                 : opt.oor_fill ? (uint8_t)oor_rng() : 0;
+            if (x.nbytes == 1 && !x.addr[0] && opt.oor_fill)
+                for (uint32_t i = 1; i < x.slot; ++i)
+                    v[i] = (uint8_t)oor_rng();
             memcpy(lds.data() + x.lds, v, x.slot);   // a 1-byte load fills a dword, zero-extended
         }
     }

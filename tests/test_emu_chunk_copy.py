@@ -6,6 +6,9 @@ buffers, every LDS read after the wait that retires its load, and no load in
 flight when a wave ends ("Asynchronous Copies", section "A Global-to-Shared
 Copy", the paragraph on the copy's operands).
 
+Policies 2 and 3 also leave random bytes, instead of zeros, in the LDS slots
+of lanes whose loads fail the range check: no result may depend on them.
+
 The last tests plant mistakes in what the emulator is given (a wait count one
 too small, buffers registered one chunk short) and require it to report them."""
 import numpy as np
@@ -70,7 +73,7 @@ def _combos_inputs():
         ignore_src=torch.tensor([c[1] for c in combos], dtype=torch.uint8))
 
 
-@pytest.mark.parametrize("policy", [0, 1])
+@pytest.mark.parametrize("policy", [0, 1, 2, 3])
 def test_operand_combinations_all_paths(policy):
     inp = _combos_inputs()
     for stages in (1, 2, 3):
@@ -85,7 +88,7 @@ def test_sizes_and_stages(n):
     stage_list = range(1, 9) if n <= 1000 else (1, 2, 4, 8)
     for stages in stage_list:
         off = (0, 0) if stages % 2 else (3, 2)
-        _check(inp, stages, 0, *off, policy=stages % 2, seed=stages)
+        _check(inp, stages, 0, *off, policy=stages % 4, seed=stages)
 
 
 def test_tiles_per_block():
@@ -219,6 +222,6 @@ def test_random_configurations():
         meta = [m if u else None for m, u in zip(meta, use)]
         expected = oracle.chunk_copy(src, dst, *meta, chunk_bytes=width)
         plan = emu.chunk_copy(src, dst, *meta, chunk_bytes=width, stages=stages,
-                              tiles_per_block=tpb, policy=i % 2, seed=i)
+                              tiles_per_block=tpb, policy=i % 4, seed=i)
         assert np.array_equal(dst, expected), (i, width, n, stages, tpb, src_off, dst_off, use,
                                                plan.path)
