@@ -45,13 +45,16 @@ def parse():
     ap.add_argument("--tiles-per-block", type=int, default=0,
                     help="consecutive tiles per workgroup (0: the library default)")
     ap.add_argument("--quick", action="store_true", help="headline only: no sweep, no extra rows")
-    ap.add_argument("--mode", choices=("bench", "stages", "sweep", "occupancy", "map2d", "align"),
+    ap.add_argument("--mode", choices=("bench", "stages", "sweep", "occupancy", "map2d", "align",
+                                       "strides"),
                     default="bench",
                     help="stages: only the maps at 1-4 stages; sweep: only the 36-point stage/tile "
                          "sweep (both for hardware-counter passes); occupancy: scale2 bandwidth "
                          "against the bound on resident workgroups per CU; map2d: only the 2-D "
                          "map with its default box (for counter passes); align: scale2 bandwidth "
-                         "against the offsets of in and out from a 128-byte line, both policies")
+                         "against the offsets of in and out from a 128-byte line, both policies; "
+                         "strides: 2-D map bandwidth against the source's row padding and the "
+                         "run width")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU work: read the rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE outputs "
@@ -427,6 +430,34 @@ def chunk_copy_row(tp, workloads, torch, np, dev):
     return out
 
 
+def strides_mode(args):
+    """scale2 over a 16384 x 16384 window of a source whose rows carry 0-8 KiB
+    of padding, into a dense destination, with one-row boxes 256-2048 floats
+    wide and runs of 1 and 2 boxes (2 stages), in interleaved rounds."""
+    import torch
+    import software_pipelining_amd as tp
+    dev = torch.device("cuda:0")
+    R = C = 16384
+    pads = [0, 4, 16, 32, 48, 64, 96, 128, 192, 256, 512, 1024, 2048]
+    widths = [256, 512, 1024, 2048]
+    src = torch.empty(R * (C + max(pads)), device=dev).uniform_(-1, 1)
+    dst = torch.empty(R, C, device=dev)
+    gpu_warmup(lambda: tp.map_2d(src[:R * C].view(R, C), dst, "scale2", 1, 1024, 2, 0), 300)
+    res = {}
+    for _ in range(2):
+        for pad in pads:
+            s = src[:R * (C + pad)].view(R, C + pad)[:, :C]
+            for w in widths:
+                for T in (1, 2):
+                    f = lambda: tp.map_2d(s, dst, "scale2", 1, w, 2, T)
+                    ms = time_region(f, 2, args.steps)
+                    res.setdefault((pad, w, T), []).append(8 * R * C / (ms / args.steps * 1e-3) / 1e9)
+    for pad in pads:
+        log(f"strides pad {pad} floats ({4 * pad} B): " + " ".join(
+            f"1x{w} T{T} {median(res[(pad, w, T)]):.0f}" for w in widths for T in (1, 2)))
+    torch.cuda.synchronize()
+
+
 def align_mode(args):
     """scale2 over 2^28 with in and out at byte offsets from a 256-byte
     boundary, under the library's realignment and under the pages' 4-byte
@@ -484,6 +515,9 @@ def main():
         return
     if args.mode == "align":
         align_mode(args)
+        return
+    if args.mode == "strides":
+        strides_mode(args)
         return
 
     import numpy as np
