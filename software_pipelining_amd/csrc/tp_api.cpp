@@ -27,12 +27,6 @@ int hip_failure(hipError_t e)
     return TP_ERR_HIP;
 }
 
-// gfx950 only: the arch name is "gfx950" optionally followed by ":feature..."
-bool is_gfx950(const char *arch)
-{
-    return strncmp(arch, "gfx950", 6) == 0 && (arch[6] == '\0' || arch[6] == ':');
-}
-
 int query_device(int device, int64_t *lds_budget)
 {
     if (device < 0 || device >= kMaxDevices)
@@ -53,7 +47,7 @@ int query_device(int device, int64_t *lds_budget)
     e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, device);
     if (e != hipSuccess)
         return hip_failure(e);
-    DeviceInfo info{true, is_gfx950(prop.gcnArchName) ? TP_OK : TP_ERR_UNSUPPORTED_DEVICE, lds};
+    DeviceInfo info{true, tp::arch_status(prop.gcnArchName), lds};
     {
         std::lock_guard<std::mutex> lock(g_mutex);
         g_devices[device] = info;

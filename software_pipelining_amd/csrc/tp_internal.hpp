@@ -209,6 +209,10 @@ int plan_chunk_copy(uintptr_t src, uintptr_t dst, int64_t n_chunks, int chunk_by
                     uintptr_t pred, uintptr_t src_size, uintptr_t ignore_src, int stages,
                     int tiles_per_block, int64_t lds_budget, tp_plan *plan);
 
+// TP_OK for a device whose architecture name is gfx950 (optionally followed by
+// ":feature..." suffixes), TP_ERR_UNSUPPORTED_DEVICE for any other name.
+int arch_status(const char *arch);
+
 // Horner coefficients c_k = RN(1/(k+1)), k = 0..31.
 void horner32_coefficients(float c[32]);
 

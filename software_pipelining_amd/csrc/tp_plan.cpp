@@ -359,6 +359,13 @@ void horner32_coefficients(float c[32])
         c[k] = 1.0f / (float)(k + 1);
 }
 
+int arch_status(const char *arch)
+{
+    return arch && strncmp(arch, "gfx950", 6) == 0 && (arch[6] == '\0' || arch[6] == ':')
+               ? TP_OK
+               : TP_ERR_UNSUPPORTED_DEVICE;
+}
+
 MapParams map_params(const tp_plan &plan, const float *in, float *out, int64_t n)
 {
     MapParams p;

@@ -77,4 +77,8 @@ int emu_row_shift(const float *a, float *b, int64_t rows, const emu::Options *o,
     return emu::launch(plan, *o, body, err, errlen);
 }
 
+// The library's device check on an architecture name, as the device would
+// report it (the check itself needs no device).
+int emu_arch_status(const char *arch) { return tp::arch_status(arch); }
+
 }  // extern "C"

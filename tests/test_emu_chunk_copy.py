@@ -225,3 +225,18 @@ def test_random_configurations():
                               tiles_per_block=tpb, policy=i % 4, seed=i)
         assert np.array_equal(dst, expected), (i, width, n, stages, tpb, src_off, dst_off, use,
                                                plan.path)
+
+
+def test_device_check_accepts_only_gfx950():
+    # the library's check of a device's architecture name: gfx950 with or
+    # without feature suffixes passes, any other name is TP_ERR_UNSUPPORTED_DEVICE
+    import ctypes
+    f = emu.lib().emu_arch_status
+    f.argtypes = [ctypes.c_char_p]
+    f.restype = ctypes.c_int
+    for name in (b"gfx950", b"gfx950:sramecc+:xnack-", b"gfx950:xnack+"):
+        assert f(name) == 0, name
+    for name in (b"gfx942", b"gfx942:sramecc+:xnack-", b"gfx9500", b"gfx95", b"gfx90a", b"",
+                 b"gfx1100", b"sm_90"):
+        assert f(name) == 5, name
+    assert f(None) == 5
