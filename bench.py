@@ -401,9 +401,10 @@ def chunk_copy_algorithmic_bytes(pred, src_size, ignore_src) -> int:
 
 
 def chunk_copy_row(tp, workloads, torch, np, dev):
-    """The predicated chunk copy over 2^26 chunks at 1, 2 and 4 stages: GB/s on
-    the exact algorithmic bytes of this instance, and bit-exact parity of the
-    whole destination with the oracle."""
+    """The predicated chunk copy over 2^26 chunks at 1, 2 and 4 stages with the
+    default run of 64 tiles per workgroup, and at 2 stages with runs of 1, 2
+    and 8 tiles: GB/s on the exact algorithmic bytes of this instance, and
+    bit-exact parity of the whole destination with the oracle."""
     import oracle
     nc = 1 << 26
     inp = workloads.chunk_copy_inputs(nc, seed=3)
@@ -414,17 +415,18 @@ def chunk_copy_row(tp, workloads, torch, np, dev):
     src = inp.src.reshape(-1).to(dev)
     meta = [m.to(dev) for m in (inp.pred, inp.src_size, inp.ignore_src)]
     out = {"n_chunks": nc, "algorithmic_bytes": alg, "bytes_per_chunk": round(alg / nc, 3)}
-    for stages in (1, 2, 4):
+    for stages, tpb in ((1, 0), (2, 0), (4, 0), (2, 1), (2, 2), (2, 8)):
         dst = inp.dst_init.reshape(-1).to(dev)
-        f = lambda: tp.chunk_copy(src, dst, *meta, stages=stages)
+        f = lambda: tp.chunk_copy(src, dst, *meta, stages=stages, tiles_per_block=tpb)
         f()
         torch.cuda.synchronize()
         parity = bool(torch.equal(dst, exp_d))          # the copy is idempotent: re-running it
         per, _ = time_launches(f, 3, 20)                 # rewrites the same bytes
         us = median(per) * 1e3
-        out[f"S{stages}"] = {"us": round(us, 1), "GBs": round(alg / (us * 1e-6) / 1e9, 1),
-                             "pct_peak": round(100 * alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
-                             "parity": parity}
+        key = f"S{stages}" if tpb == 0 else f"S{stages}_T{tpb}"
+        out[key] = {"us": round(us, 1), "GBs": round(alg / (us * 1e-6) / 1e9, 1),
+                    "pct_peak": round(100 * alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
+                    "parity": parity}
         del dst
     log(f"chunk_copy: {out}")
     return out
