@@ -46,7 +46,7 @@ def parse():
                     help="consecutive tiles per workgroup (0: the library default)")
     ap.add_argument("--quick", action="store_true", help="headline only: no sweep, no extra rows")
     ap.add_argument("--mode", choices=("bench", "stages", "sweep", "occupancy", "map2d", "align",
-                                       "strides"),
+                                       "strides", "chunk"),
                     default="bench",
                     help="stages: only the maps at 1-4 stages; sweep: only the 36-point stage/tile "
                          "sweep (both for hardware-counter passes); occupancy: scale2 bandwidth "
@@ -54,7 +54,8 @@ def parse():
                          "map with its default box (for counter passes); align: scale2 bandwidth "
                          "against the offsets of in and out from a 128-byte line, both policies; "
                          "strides: 2-D map bandwidth against the source's row padding and the "
-                         "run width")
+                         "run width; chunk: only the chunk copy (default run and runs of 2, 2 "
+                         "stages) and the runtime's 1 GiB copy, for counter passes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU work: read the rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE outputs "
@@ -460,6 +461,33 @@ def strides_mode(args):
     torch.cuda.synchronize()
 
 
+def chunk_mode(args):
+    """The chunk-copy workload at 2 stages with the default run of 64 tiles and
+    with runs of 2, `steps` times each, then the runtime's 1 GiB copy (the
+    traffic counters' calibration)."""
+    import torch
+    import software_pipelining_amd as tp
+    from software_pipelining_amd import workloads
+    dev = torch.device("cuda:0")
+    nc = 1 << 26
+    inp = workloads.chunk_copy_inputs(nc, seed=3)
+    alg = chunk_copy_algorithmic_bytes(inp.pred, inp.src_size, inp.ignore_src)
+    src = inp.src.reshape(-1).to(dev)
+    dst = inp.dst_init.reshape(-1).to(dev)
+    meta = [m.to(dev) for m in (inp.pred, inp.src_size, inp.ignore_src)]
+    gpu_warmup(lambda: tp.chunk_copy(src, dst, *meta, stages=2))
+    for tpb in (0, 2):
+        per, _ = time_launches(lambda: tp.chunk_copy(src, dst, *meta, stages=2, tiles_per_block=tpb),
+                               1, args.steps)
+        log(f"chunk copy S2 T{tpb or 64}: {median(per) * 1e3:.1f} us, "
+            f"{alg / (median(per) * 1e-3) / 1e9:.0f} GB/s on {alg} algorithmic bytes")
+    flat = torch.empty(1 << 28, device=dev)
+    out = torch.empty_like(flat)
+    for _ in range(3):
+        out.copy_(flat)
+    torch.cuda.synchronize()
+
+
 def align_mode(args):
     """scale2 over 2^28 with in and out at byte offsets from a 256-byte
     boundary, under the library's realignment and under the pages' 4-byte
@@ -520,6 +548,9 @@ def main():
         return
     if args.mode == "strides":
         strides_mode(args)
+        return
+    if args.mode == "chunk":
+        chunk_mode(args)
         return
 
     import numpy as np
