@@ -81,7 +81,8 @@ class Options(ctypes.Structure):
     _fields_ = [("policy", ctypes.c_int), ("wait_bias", ctypes.c_int), ("seed", ctypes.c_uint64),
                 ("lds_base", ctypes.c_uint32), ("regions", ctypes.POINTER(Region)),
                 ("n_regions", ctypes.c_int), ("blocks", ctypes.POINTER(ctypes.c_int64)),
-                ("n_blocks", ctypes.c_int), ("oor_fill", ctypes.c_int)]
+                ("n_blocks", ctypes.c_int), ("oor_fill", ctypes.c_int),
+                ("drop_barriers", ctypes.c_int)]
 
 
 class EmulationError(AssertionError):
@@ -113,8 +114,10 @@ def _region(r):
 def _options(regions, policy, seed, wait_bias, lds_base, blocks):
     regs = (Region * len(regions))(*[_region(r) for r in regions])
     # policy 0/1: loads land at retirement / at issue; + 2: out-of-range lanes
-    # leave random bytes in LDS instead of zeros
-    o = Options(policy & 1, wait_bias, seed, lds_base, regs, len(regions), None, 0, policy >> 1)
+    # leave random bytes in LDS instead of zeros; + 4: barriers do nothing (a
+    # planted mistake)
+    o = Options(policy & 1, wait_bias, seed, lds_base, regs, len(regions), None, 0,
+                (policy >> 1) & 1, (policy >> 2) & 1)
     keep = [regs]
     if blocks is not None:
         arr = (ctypes.c_int64 * len(blocks))(*blocks)

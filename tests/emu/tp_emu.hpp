@@ -74,6 +74,7 @@ struct Options {
     int oor_fill;        // what an out-of-range lane's load leaves in its LDS slot:
                          // 0 zeros (measured on the MI355X), 1 random bytes (the
                          // kernels must not depend on it)
+    int drop_barriers;   // a planted mistake: workgroup barriers do nothing
 };
 
 struct Fail : std::runtime_error {
@@ -315,7 +316,7 @@ class Emulator {
                 retire(w);
             break;
         }
-        case K_BARRIER: w.at_barrier = true; break;
+        case K_BARRIER: w.at_barrier = !opt.drop_barriers; break;
         case K_DONE:
             for (const VmOp &op : w.vm)
                 if (op.load)

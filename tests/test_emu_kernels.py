@@ -286,6 +286,23 @@ def test_planted_short_wait_is_reported(case):
             emu.row_shift(x[:256].reshape(64, 4), y[:256].reshape(64, 4), wait_bias=1)
 
 
+@pytest.mark.parametrize("case", ["barrier", "role_split", "row_shift"])
+def test_planted_missing_barriers_are_reported(case):
+    # the schedules whose lanes read bytes other waves loaded: without their
+    # barriers, a wave reads LDS another wave wrote (or reloads LDS another
+    # wave still reads) with nothing ordering the two
+    x = _floats(3 * 1024 + 8, seed=3)
+    drop = 4
+    with pytest.raises(emu.EmulationError, match="no barrier|no load of this workgroup wrote"):
+        if case == "barrier":
+            emu.pipelined_map(x, _out(x.size, 1), "scale2", 1024, 2, 2, align="words", policy=drop)
+        elif case == "role_split":
+            emu.pipelined_map(x, _out(x.size), "scale2", 1024, 2, 2, schedule="role_split",
+                              policy=drop)
+        else:
+            emu.row_shift(x[:512].reshape(128, 4), _out(512).reshape(128, 4), policy=drop)
+
+
 def test_planted_short_buffers_are_reported():
     x = _floats(2 * 1024, seed=2)
     y = _out(x.size)
