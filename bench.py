@@ -794,6 +794,31 @@ def extra_rows(args, tp, workloads, torch, np, dev, x_host, xbuf, y):
     log(f"horner32: {hr}")
     del xh, yh
 
+    # memory-bound map (scale2 over the step's input) at 1/2/4 stages: the
+    # library's launch, and tile 1024 in runs of 8 at 2 workgroups (8 waves)
+    # per CU, where other waves no longer hide a wave's loads; interleaved rounds
+    xm = xbuf[:n]
+    sgroups = [(256, 0, 0), (1024, 8, 2)]
+    sconf = [(tile, tpb, cap, S) for tile, tpb, cap in sgroups for S in (1, 2, 4)]
+    srun = lambda tile, tpb, cap, S: tp.pipelined_map(xm, y, "scale2", tile, S, tpb, resident_cap=cap)
+    gpu_warmup(lambda: srun(256, 0, 0, 2))
+    st = {c: [] for c in sconf}
+    for _ in range(4):
+        for c in sconf:
+            per, _ = time_launches(lambda: srun(*c), 1, 4)
+            st[c] += per
+    sr = {}
+    for tile, tpb, cap in sgroups:
+        key = f"tile{tile}_T{tpb or 'default'}" + (f"_{cap}wg_per_cu" if cap else "_library_bound")
+        for S in (1, 2, 4):
+            t = median(st[(tile, tpb, cap, S)]) * 1e-3
+            sr[f"{key}_S{S}"] = {"GBs": round(8 * n / t / 1e9, 1), "us": round(t * 1e6, 1)}
+        sr[f"{key}_speedup_S2_over_S1"] = round(sr[f"{key}_S1"]["us"] / sr[f"{key}_S2"]["us"], 3)
+        sr[f"{key}_speedup_S4_over_S1"] = round(sr[f"{key}_S1"]["us"] / sr[f"{key}_S4"]["us"], 3)
+    sr["parity"] = bool(sampled_parity(x_host, y, "scale2"))
+    rows["scale2_stages"] = sr
+    log(f"scale2 stages: {sr}")
+
     rows["map_2d"] = map_2d_row(tp, workloads, torch, np, dev, y)
 
     # predicated chunk copy: 2^26 chunks
