@@ -1,10 +1,11 @@
 // CPU emulator of the library's kernel bodies (test infrastructure): the
-// emulated engine and the scheduler. tp_emu_*.cpp instantiate the bodies.
+// emulated engine and the scheduler.
 //
 // The kernel bodies of libtilepipe are templates on an engine type. The
-// library instantiates them with the gfx950 engine; this file instantiates the
-// very same source with an emulated engine and runs a planned launch on the
-// host, one workgroup after another. Every lane is a fiber; the lanes of a
+// library instantiates them with the gfx950 engine; tp_emu_*.cpp instantiate
+// the very same source with the emulated engine below and run a planned launch
+// on the host, one workgroup after another (one launch at a time per process:
+// the scheduler's state is global). Every lane is a fiber; the lanes of a
 // wave run in lock-step from one engine call to the next, and each engine call
 // is executed once for the whole wave, as the hardware executes one
 // instruction for 64 lanes. At every call the emulator checks what a GPU run
@@ -556,12 +557,9 @@ struct EmuEngine {
     }
 };
 
-inline int report(const char *what, char *err, int errlen)
-{
-    if (err && errlen > 0)
-        snprintf(err, errlen, "%s", what);
-    return 1;
-}
+// Status of an entry point: a tp_status from planning, 0, or these.
+constexpr int kViolation = -1;       // `err` holds the first violation
+constexpr int kNotInstantiated = -2; // that kernel instance is not compiled into the emulator
 
 // Calls f(std::integral_constant<int, V>{}) for the V in the list equal to v;
 // false when none is (that kernel instance is not compiled in).
@@ -582,12 +580,10 @@ int launch(const tp_plan &plan, const Options &opt, Body body, char *err, int er
         return 0;
     } catch (const Fail &f) {
         g_emu = nullptr;
-        return report(f.what(), err, errlen) ? -1 : 0;
+        if (err && errlen > 0)
+            snprintf(err, errlen, "%s", f.what());
+        return kViolation;
     }
 }
-
-// Status of an entry point: a tp_status from planning, or these.
-constexpr int kViolation = -1;       // `err` holds the first violation
-constexpr int kNotInstantiated = -2; // that kernel instance is not compiled into the emulator
 
 }  // namespace emu
