@@ -819,6 +819,19 @@ def extra_rows(args, tp, workloads, torch, np, dev, x_host, xbuf, y):
     rows["scale2_stages"] = sr
     log(f"scale2 stages: {sr}")
 
+    # vendor kernels on the same 1 GiB buffers, for context: a read-only
+    # reduction (torch.sum reads 1 GiB) and a write-only fill (1 GiB written)
+    xr = xbuf[:n]
+    gpu_warmup(lambda: xr.sum())
+    per_r, _ = time_launches(lambda: xr.sum(), 2, 10)
+    per_w, _ = time_launches(lambda: y.fill_(1.0), 2, 10)
+    rows["vendor_context"] = {
+        "torch_sum_read_only_GBs": round(4 * n / (median(per_r) * 1e-3) / 1e9, 1),
+        "torch_fill_write_only_GBs": round(4 * n / (median(per_w) * 1e-3) / 1e9, 1),
+        "note": "torch.sum over the step's 1 GiB input and fill_ of its 1 GiB output, "
+                "bytes moved per second; the runtime's 1 GiB copy is copy_ceiling_GBs"}
+    log(f"vendor context: {rows['vendor_context']}")
+
     rows["map_2d"] = map_2d_row(tp, workloads, torch, np, dev, y)
 
     # predicated chunk copy: 2^26 chunks
