@@ -74,10 +74,12 @@ def test_config4_predicated_chunk_copy(cuda_device):
     exp_d = torch.from_numpy(exp.reshape(-1)).to(cuda_device)
     src = inp.src.reshape(-1).to(cuda_device)
     meta = [m.to(cuda_device) for m in (inp.pred, inp.src_size, inp.ignore_src)]
-    for stages in (1, 2, 4):
+    # the launches the benchmark times: the default run of 64 tiles at 1, 2 and
+    # 4 stages, and runs of 1, 2 and 8 tiles at 2 stages
+    for stages, tpb in ((1, 0), (2, 0), (4, 0), (2, 1), (2, 2), (2, 8)):
         dst = inp.dst_init.reshape(-1).to(cuda_device)
-        tp.chunk_copy(src, dst, *meta, stages=stages)
-        assert_equal_on_device(dst, exp_d, f"config 4 S={stages}")
+        tp.chunk_copy(src, dst, *meta, stages=stages, tiles_per_block=tpb)
+        assert_equal_on_device(dst, exp_d, f"config 4 S={stages} T={tpb}")
 
 
 def test_config5_horner32(cuda_device):
