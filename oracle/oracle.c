@@ -121,6 +121,11 @@ void oracle_map_2d(const float *src, int64_t src_stride, float *dst, int64_t dst
  * If this is zero on a workload, a flush-to-zero mode on either side could not
  * have changed any result there. The product is formed in double, where the
  * product of two binary32 values is exact.
+ * The check on y cannot fire for finite inputs: y = fma(y', x, c_k) with
+ * c_k >= 2^-5 is below 2^-126 only if y'x cancels c_k, which needs
+ * |y'x| > 2^-6; both terms then lie on a grid no finer than 2^-53, so their
+ * sum is zero or at least 2^-53. It stays as a guard; the product count is
+ * the one that inputs such as subnormal x reach (31 steps for any subnormal x).
  */
 int64_t oracle_horner32_subnormal_steps(const float *in, int64_t lo, int64_t hi)
 {

@@ -10,12 +10,9 @@ import torch
 # inline-asm buffer instructions, which then read stale SGPRs (a VALU-written
 # SGPR needs 5 wait states before a vector-memory instruction reads it). The
 # asm blocks now carry those wait states and a static check of the built code
-# object enforces them (test_isa_hazards.py). A case that faulted again after
-# a first fix stays off the GPU for a while before the fix of its shown cause
-# gets its own GPU run; its kernel source runs under the CPU emulator meanwhile
-# (tests/test_emu_chunk_copy.py).
-CHUNK_COPY_GPU_SKIP = ("chunk copy kept off the GPU: it faulted twice before the descriptor "
-                       "wait-state hazard was found and fixed, and that fix has not had its GPU run")
+# object enforces them (test_isa_hazards.py); its kernel source also runs under
+# the CPU emulator (tests/test_emu_chunk_copy.py). None means the GPU tests run.
+CHUNK_COPY_GPU_SKIP = None
 
 GUARD = 64                      # sentinel words before and after every buffer
 SENTINEL = 0x7FC0DEAD           # a NaN pattern none of the tests' results contain

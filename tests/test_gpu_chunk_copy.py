@@ -36,6 +36,8 @@ def _run(dev, inp, stages, tpb, src_off=0, dst_off=0, use=(True, True, True)):
     dst = _dst(n, dev, dst_off)
     metas = [m if u else None for m, u in zip((inp.pred, inp.src_size, inp.ignore_src), use)]
     devm = [_meta(m, dev) for m in metas]
+    print(f"chunk_copy n={n} S={stages} T={tpb} src+{4 * src_off}B dst+{4 * dst_off}B use={use}",
+          flush=True)
     path = tp.chunk_copy(src.tensor, dst.tensor, *(d[1] for d in devm), stages=stages,
                          tiles_per_block=tpb)
     expected = oracle.chunk_copy(inp.src.numpy(), inp.dst_init.numpy(),
@@ -115,6 +117,7 @@ def test_chunk_copy_in_place(cuda_device):
     for stages in (1, 2, 3):
         buf = to_device(inp.src.reshape(-1), cuda_device)
         metas = [to_device(m, cuda_device) for m in (inp.pred, inp.src_size, inp.ignore_src)]
+        print(f"chunk_copy in place n={n} S={stages}", flush=True)
         tp.chunk_copy(buf.tensor, buf.tensor, *(m.tensor for m in metas), stages=stages)
         assert_bits_equal(buf.tensor, expected, f"in place S={stages}")
         assert buf.guards_intact()
@@ -153,6 +156,7 @@ def test_narrow_chunks(cuda_device, width):
                     dst = Guarded(n * width, torch.uint8, cuda_device, fill_word=DEADBEEF)
                     devm = [_meta(None if m is None else torch.from_numpy(m), cuda_device)
                             for m in metas]
+                    print(f"chunk_copy W={width} n={n} S={stages} T={tpb} use={use}", flush=True)
                     path = tp.chunk_copy(src.tensor, dst.tensor, *(d[1] for d in devm),
                                          stages=stages, tiles_per_block=tpb, chunk_bytes=width)
                     assert path == tp.Path.SCALAR

@@ -78,6 +78,7 @@ def test_config4_predicated_chunk_copy(cuda_device):
     # 4 stages, and runs of 1, 2 and 8 tiles at 2 stages
     for stages, tpb in ((1, 0), (2, 0), (4, 0), (2, 1), (2, 2), (2, 8)):
         dst = inp.dst_init.reshape(-1).to(cuda_device)
+        print(f"config 4 chunk_copy n=2^26 S={stages} T={tpb}", flush=True)
         tp.chunk_copy(src, dst, *meta, stages=stages, tiles_per_block=tpb)
         assert_equal_on_device(dst, exp_d, f"config 4 S={stages} T={tpb}")
 

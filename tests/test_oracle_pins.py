@@ -190,6 +190,48 @@ def test_horner_within_error_bound_of_exact_polynomial():
     assert abs(float(got[0]) - float(sum(Fraction((-1) ** (31 - k), k + 1) for k in range(32)))) < 1e-5
 
 
+def _subnormal_steps_exact(x: np.float32, c) -> int:
+    """Independent count for one input: the exact products y*x of the chain
+    (Fractions, so nothing rounds) that are nonzero and below 2^-126, with y
+    advanced by the exact-rational fma."""
+    tiny = Fraction(1, 2 ** 126)
+    y, count = np.float32(0.0), 0
+    for k in range(32):
+        prod = Fraction(float(y)) * Fraction(float(x))
+        if prod != 0 and abs(prod) < tiny:
+            count += 1
+        y = fma_f32(y, x, c[k])
+    return count
+
+
+def test_horner_subnormal_counter_positive_controls():
+    # Closed forms. For a tiny x the products y*x are far below half an ulp of
+    # c_k >= 2^-5, so every step returns y = c_k and step k >= 1 forms the
+    # product c_{k-1} * x:
+    #   x subnormal (1e-39, 2^-149, either sign): all 31 products from k = 1 on;
+    #   x = 2^-122: c_{k-1} * 2^-122 < 2^-126 exactly when c_{k-1} < 1/16, i.e.
+    #     k = 17..31 (k = 16 gives exactly 2^-126, the smallest normal): 15;
+    #   x = 2^-120 or larger, x = 0: no product below 2^-126: 0.
+    cases = {np.float32(1e-39): 31, np.float32(-1e-39): 31, np.float32(2.0 ** -149): 31,
+             np.float32(2.0 ** -122): 15, np.float32(-(2.0 ** -122)): 15,
+             np.float32(2.0 ** -120): 0, np.float32(0.0): 0, np.float32(-0.0): 0,
+             np.float32(0.5): 0, np.float32(-1.0): 0}
+    for x, n in cases.items():
+        assert oracle.horner32_subnormal_steps(np.array([x], np.float32)) == n, float(x)
+    # the counts add over inputs
+    xs = np.array(list(cases), np.float32)
+    assert oracle.horner32_subnormal_steps(xs) == sum(cases.values())
+    # brute force against the exact-rational chain on a sweep of binades
+    c = _coeffs_exact()
+    rng = np.random.default_rng(5)
+    sweep = [np.float32(s * m * 2.0 ** e) for e in range(-150, -110, 3)
+             for s, m in ((1, 1.0), (-1, 1.37), (1, 1.9))]
+    sweep += [np.float32(v) for v in rng.uniform(-1, 1, 20)]
+    for x in sweep:
+        assert oracle.horner32_subnormal_steps(np.array([x], np.float32)) == \
+            _subnormal_steps_exact(x, c), float(x)
+
+
 def test_horner_workload_sample_has_no_subnormal_steps():
     # rounding reading: the workload's inputs never produce a subnormal
     # intermediate, so flush-to-zero modes could not change a result on it
