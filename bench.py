@@ -24,10 +24,6 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 FP32_VALU_PEAK_TFLOPS = 78.6   # unpacked v_fma_f32: 256 CU x 128 lanes x 2 FLOP x 2.4 GHz
-# The chunk copy is kept off the GPU until the fix of the memory fault it made
-# has had its own GPU run (tests/gpu_util.py gives the cause); its row is then
-# reported as not run.
-CHUNK_COPY_TIMED = False
 METRIC = "achieved HBM GB/s (read+write) and % of MI355X peak, pipelined map, 1 GPU"
 
 
@@ -54,14 +50,18 @@ def parse():
                          "map with its default box (for counter passes); align: scale2 bandwidth "
                          "against the offsets of in and out from a 128-byte line, both policies; "
                          "strides: 2-D map bandwidth against the source's row padding and the "
-                         "run width; chunk: only the chunk copy (default run and runs of 2, 2 "
-                         "stages) and the runtime's 1 GiB copy, for counter passes")
+                         "run width; chunk: only the chunk copy (the points of "
+                         "CHUNK_COUNTER_POINTS, in order) and the runtime's 1 GiB copy, for "
+                         "counter passes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU work: read the rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE outputs "
                          "of two runs of `bench.py --quick --no-cpu-baseline` (defaults otherwise), "
                          "scale each counter by what it reads for the runtime's 1 GiB copy, and "
                          "store the step's HBM bytes per launch in profiles/traffic.json")
+    ap.add_argument("--record-chunk-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU work: the same for two runs of `bench.py --mode chunk`: store the "
+                         "HBM bytes per launch of each point of CHUNK_COUNTER_POINTS")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline")
     return ap.parse_args()
@@ -141,11 +141,18 @@ MAP_KERNEL_SOURCES = ["software_pipelining_amd/csrc/" + f for f in (
     "tp_plan.cpp", "tp_api.cpp")] + ["include/tilepipe.h", "software_pipelining_amd/build.py"]
 
 
-def kernel_source_hash() -> str:
-    """Hash of what builds and launches the map kernel: a stored hardware-counter
-    reading is only reported while it still describes the kernel being run."""
+# The same for the chunk copy.
+CHUNK_KERNEL_SOURCES = ["software_pipelining_amd/csrc/" + f for f in (
+    "tp_engine.hpp", "tp_internal.hpp", "tp_chunk_copy.hpp", "tp_chunk_copy.hip", "tp_plan.cpp",
+    "tp_api.cpp")] + ["include/tilepipe.h", "software_pipelining_amd/build.py"]
+
+
+def kernel_source_hash(sources=None) -> str:
+    """Hash of what builds and launches a kernel (the map's by default): a stored
+    hardware-counter reading is only reported while it still describes the
+    kernel being run."""
     h = hashlib.sha256()
-    for name in MAP_KERNEL_SOURCES:
+    for name in sources or MAP_KERNEL_SOURCES:
         with open(os.path.join(ROOT, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -155,9 +162,10 @@ def step_traffic_key(n: int, tile: int, stages: int, tiles_per_block: int) -> st
     return f"map_scale2_n{n}_t{tile}_s{stages}_T{tiles_per_block}"
 
 
-def _counter_rows(directory: str, counter: str):
+def _counter_rows(directory: str, counter: str, with_ids: bool = False):
     """(kernel name, grid size, value) of every dispatch in the rocprofv3
-    counter-collection CSVs under `directory`."""
+    counter-collection CSVs under `directory` (with_ids: (dispatch id, name,
+    grid, value), in dispatch order)."""
     import csv
     import glob
     rows = []
@@ -165,10 +173,22 @@ def _counter_rows(directory: str, counter: str):
         with open(path, newline="") as f:
             for r in csv.DictReader(f):
                 if r.get("Counter_Name") == counter:
-                    rows.append((r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"])))
+                    rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["Grid_Size"]),
+                                 float(r["Counter_Value"])))
     if not rows:
         raise SystemExit(f"no {counter} rows under {directory}")
-    return rows
+    rows.sort()
+    return rows if with_ids else [r[1:] for r in rows]
+
+
+def _copy_calibration_kib(rows):
+    """Counter KiB of the runtime's 1 GiB copy: the copyBuffer dispatches with
+    the largest grid (it reads and writes exactly 2^30 bytes)."""
+    copies = [r for r in rows if "copyBuffer" in r[0]]
+    if not copies:
+        raise SystemExit("no runtime copy dispatch among the counter rows")
+    big = max(g for _, g, _ in copies)
+    return median([v for _, g, v in copies if g == big])
 
 
 def record_traffic(fetch_dir: str, write_dir: str, path: str | None = None):
@@ -182,11 +202,7 @@ def record_traffic(fetch_dir: str, write_dir: str, path: str | None = None):
     out = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _counter_rows(d, counter)
-        copies = [r for r in rows if "copyBuffer" in r[0]]
-        if not copies:
-            raise SystemExit(f"no runtime copy dispatch in {d}")
-        big = max(g for _, g, _ in copies)
-        copy_kib = median([v for _, g, v in copies if g == big])
+        copy_kib = _copy_calibration_kib(rows)
         maps = [v for k, _, v in rows if "map_kernel<0, 2, 1, true, true>" in k]
         if not maps:
             raise SystemExit(f"no map_kernel<scale2, S=2, L=1, x4, x4> dispatch in {d}")
@@ -219,7 +235,54 @@ def record_traffic(fetch_dir: str, write_dir: str, path: str | None = None):
         f"{(fetch + write) / alg:.6f} x the algorithmic {alg} B")
 
 
-def stored_traffic(key: str, path: str | None = None):
+def chunk_traffic_key(operands: str, stages: int, tiles_per_block: int) -> str:
+    """Key of a chunk-copy launch over the 2^26-chunk workload, by the ring and
+    run the planner chose."""
+    return f"chunk_copy_n67108864_{operands}_s{stages}_T{tiles_per_block}"
+
+
+def record_chunk_traffic(fetch_dir: str, write_dir: str, path: str | None = None):
+    """HBM bytes per launch of each point of CHUNK_COUNTER_POINTS from two runs
+    of `--mode chunk`: the chunk-copy dispatches, in dispatch order, fall in
+    one group per point (one untimed launch, then the timed ones); each
+    counter is the median over a group's timed launches, calibrated on the
+    runtime's 1 GiB copy as for the map."""
+    import software_pipelining_amd as tp
+    per = {}
+    scale = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(d, counter, with_ids=True)
+        scale[counter] = float(1 << 20) / _copy_calibration_kib([r[1:] for r in rows])
+        chunk = [v for _, name, _, v in rows if "chunk_copy_kernel" in name]
+        k = len(CHUNK_COUNTER_POINTS)
+        if not chunk or len(chunk) % k:
+            raise SystemExit(f"{len(chunk)} chunk-copy dispatches in {d}: not {k} equal groups")
+        g = len(chunk) // k
+        for i in range(k):
+            per.setdefault(i, {})[counter] = median(chunk[i * g + 1:(i + 1) * g]) * scale[counter] * 1024
+    path = path or os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        table = {}
+    nc = 1 << 26
+    for i, (operands, stages, tpb) in enumerate(CHUNK_COUNTER_POINTS):
+        plan = tp.plan_chunk_copy(1 << 40, 1 << 41, nc, stages=stages, tiles_per_block=tpb)
+        key = chunk_traffic_key(operands, plan.stages, plan.tiles_per_block)
+        f, w = per[i]["FETCH_SIZE"], per[i]["WRITE_SIZE"]
+        table[key] = {"kernel_source_hash": kernel_source_hash(CHUNK_KERNEL_SOURCES),
+                      "bytes_per_launch": int(round(f + w)), "fetch_bytes": int(round(f)),
+                      "write_bytes": int(round(w)),
+                      "scale": {c: round(v, 5) for c, v in scale.items()},
+                      "source": "profiles/chunk_copy_2p26_hbm_traffic.md"}
+        log(f"traffic {key}: fetch {f / nc:.3f} B/chunk, write {w / nc:.3f} B/chunk")
+    with open(path, "w") as fh:
+        json.dump(table, fh, indent=1)
+        fh.write("\n")
+
+
+def stored_traffic(key: str, path: str | None = None, sources=None):
     path = path or os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -227,7 +290,7 @@ def stored_traffic(key: str, path: str | None = None):
     except (OSError, ValueError):
         return None
     e = d.get(key)
-    if not e or e.get("kernel_source_hash") != kernel_source_hash():
+    if not e or e.get("kernel_source_hash") != kernel_source_hash(sources):
         return None
     return e.get("bytes_per_launch")
 
@@ -401,11 +464,18 @@ def chunk_copy_algorithmic_bytes(pred, src_size, ignore_src) -> int:
     return int(3 * p.size + (keep * p).sum() + 16 * p.sum())
 
 
-def chunk_copy_row(tp, workloads, torch, np, dev):
-    """The predicated chunk copy over 2^26 chunks at 1, 2 and 4 stages with the
-    default run of 64 tiles per workgroup, and at 2 stages with runs of 1, 2
-    and 8 tiles: GB/s on the exact algorithmic bytes of this instance, and
-    bit-exact parity of the whole destination with the oracle."""
+# Launches of the chunk-copy row: (stages, tiles per workgroup; 0 = the
+# library's default run of max(1, S-1) tiles).
+CHUNK_ROW_POINTS = [(1, 0), (2, 0), (3, 0), (4, 0), (2, 2), (2, 8), (2, 64)]
+
+
+def chunk_copy_row(tp, workloads, torch, np, dev, cpu_seconds):
+    """The predicated chunk copy over 2^26 chunks: GB/s on the exact
+    algorithmic bytes of this instance at every point of CHUNK_ROW_POINTS
+    (interleaved rounds), with bit-exact parity of the whole destination
+    against the oracle at each; the same instance with every pred set (no
+    partly written destination block); 4- and 8-byte chunks; the roofline of
+    the default launch; the oracle on the host cores."""
     import oracle
     nc = 1 << 26
     inp = workloads.chunk_copy_inputs(nc, seed=3)
@@ -413,24 +483,103 @@ def chunk_copy_row(tp, workloads, torch, np, dev):
     exp = oracle.chunk_copy(inp.src.numpy(), inp.dst_init.numpy(), inp.pred.numpy(),
                             inp.src_size.numpy(), inp.ignore_src.numpy())
     exp_d = torch.from_numpy(exp.reshape(-1)).to(dev)
+    del exp
     src = inp.src.reshape(-1).to(dev)
+    dst = inp.dst_init.reshape(-1).to(dev)
     meta = [m.to(dev) for m in (inp.pred, inp.src_size, inp.ignore_src)]
-    out = {"n_chunks": nc, "algorithmic_bytes": alg, "bytes_per_chunk": round(alg / nc, 3)}
-    for stages, tpb in ((1, 0), (2, 0), (4, 0), (2, 1), (2, 2), (2, 8)):
-        dst = inp.dst_init.reshape(-1).to(dev)
-        f = lambda: tp.chunk_copy(src, dst, *meta, stages=stages, tiles_per_block=tpb)
-        f()
+    out = {"n_chunks": nc, "algorithmic_bytes": alg, "bytes_per_chunk": round(alg / nc, 3),
+           "workload": "2^26 16-byte chunks, pred ~ B(0.9), src_size uniform on {0,4,8,12,16}, "
+                       "ignore_src ~ B(0.01), destination pre-filled with 0xDEADBEEF"}
+    launch = {}
+    parity = True
+    for stages, tpb in CHUNK_ROW_POINTS:
+        dst.copy_(inp.dst_init.reshape(-1))
+        tp.chunk_copy(src, dst, *meta, stages=stages, tiles_per_block=tpb)
         torch.cuda.synchronize()
-        parity = bool(torch.equal(dst, exp_d))          # the copy is idempotent: re-running it
-        per, _ = time_launches(f, 3, 20)                 # rewrites the same bytes
-        us = median(per) * 1e3
-        key = f"S{stages}" if tpb == 0 else f"S{stages}_T{tpb}"
+        parity &= bool(torch.equal(dst, exp_d))   # the copy is idempotent: re-running it
+        launch[(stages, tpb)] = []                # rewrites the same bytes
+    gpu_warmup(lambda: tp.chunk_copy(src, dst, *meta, stages=2))
+    for _ in range(3):
+        for stages, tpb in CHUNK_ROW_POINTS:
+            per, _ = time_launches(lambda: tp.chunk_copy(src, dst, *meta, stages=stages,
+                                                         tiles_per_block=tpb), 1, 6)
+            launch[(stages, tpb)] += per
+    for stages, tpb in CHUNK_ROW_POINTS:
+        plan = tp.plan_chunk_copy(src.data_ptr(), dst.data_ptr(), nc, stages=stages,
+                                  tiles_per_block=tpb)
+        us = median(launch[(stages, tpb)]) * 1e3
+        key = f"S{stages}" + (f"_T{tpb}" if tpb else "_Tdefault")
         out[key] = {"us": round(us, 1), "GBs": round(alg / (us * 1e-6) / 1e9, 1),
                     "pct_peak": round(100 * alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1),
-                    "parity": parity}
-        del dst
+                    "ring_stages": plan.stages, "tiles_per_block": plan.tiles_per_block}
+    out["parity"] = parity
+    del exp_d
+    # the default launch (2 stages requested, runs of one tile) with every pred set
+    ones = torch.ones(nc, dtype=torch.uint8, device=dev)
+    per, _ = time_launches(lambda: tp.chunk_copy(src, dst, ones, meta[1], meta[2], stages=2), 2, 10)
+    out["pred_all_true_S2_Tdefault_us"] = round(median(per) * 1e3, 1)
+    # roofline of the default launch: the algorithmic bytes over its mean
+    # per-launch duration; HBM bytes from the counter runs while they still
+    # describe this kernel
+    dflt = tp.plan_chunk_copy(src.data_ptr(), dst.data_ptr(), nc, stages=2)
+    per, _ = time_launches(lambda: tp.chunk_copy(src, dst, *meta, stages=2), 2, 20)
+    avg = sum(per) / len(per)
+    achieved = alg / (avg * 1e-3) / 1e9
+    out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                       "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                       "traffic": stored_traffic(chunk_traffic_key("workload", dflt.stages,
+                                                                   dflt.tiles_per_block),
+                                                 sources=CHUNK_KERNEL_SOURCES),
+                       "kernel": f"chunk_copy_kernel<{dflt.stages}, 16, x4, x4>",
+                       "algorithmic_bytes_per_launch": alg, "avg_launch_us": round(avg * 1e3, 2)}
+    # 4- and 8-byte chunks: the same operand arrays over 2^26 chunks of W bytes
+    p_ = inp.pred.numpy() != 0
+    ign0 = inp.ignore_src.numpy() == 0
+    for w in (4, 8):
+        algw = int(3 * nc + (np.minimum(inp.src_size.numpy().astype(np.int64), w) * ign0 * p_).sum()
+                   + w * p_.sum())
+        sw, dw = src[:nc * w], dst[:nc * w]
+        row = {"algorithmic_bytes": algw}
+        for stages in (2, 3):
+            dw.copy_(inp.dst_init.reshape(-1)[:nc * w])
+            tp.chunk_copy(sw, dw, *meta, stages=stages, chunk_bytes=w)
+            expw = oracle.chunk_copy(inp.src.reshape(-1)[:nc * w].numpy(),
+                                     inp.dst_init.reshape(-1)[:nc * w].numpy(),
+                                     *(m.numpy() for m in (inp.pred, inp.src_size, inp.ignore_src)),
+                                     chunk_bytes=w)
+            ok = bool(torch.equal(dw.cpu(), torch.from_numpy(expw.reshape(-1))))
+            per, _ = time_launches(lambda: tp.chunk_copy(sw, dw, *meta, stages=stages, chunk_bytes=w),
+                                   2, 10)
+            us = median(per) * 1e3
+            row[f"S{stages}_Tdefault"] = {"us": round(us, 1), "GBs": round(algw / (us * 1e-6) / 1e9, 1),
+                                          "parity": ok}
+        out[f"width{w}"] = row
     log(f"chunk_copy: {out}")
+    out["cpu_baseline"] = chunk_cpu_baseline(inp, min(cpu_seconds, 10.0))
     return out
+
+
+def chunk_cpu_baseline(inp, seconds):
+    """The oracle's chunk copy (untuned) on the host cores over the same 2^26
+    chunks: whole passes for about `seconds`, GB/s on the algorithmic bytes."""
+    import oracle
+    threads = oracle.default_threads()
+    alg = chunk_copy_algorithmic_bytes(inp.pred, inp.src_size, inp.ignore_src)
+    args = [inp.src.numpy(), inp.dst_init.numpy(), inp.pred.numpy(), inp.src_size.numpy(),
+            inp.ignore_src.numpy()]
+    times = []
+    t_end = time.perf_counter() + seconds
+    while True:
+        t0 = time.perf_counter()
+        oracle.chunk_copy(*args, threads=threads)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() >= t_end:
+            break
+    t = median(times)
+    return {"value": round(alg / t / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"the full 2^26-chunk instance, {len(times)} passes in {sum(times):.1f} s, "
+                      f"median pass {t * 1e3:.1f} ms (each pass also copies the destination's "
+                      f"initial bytes into a new array)"}
 
 
 def strides_mode(args):
@@ -461,10 +610,19 @@ def strides_mode(args):
     torch.cuda.synchronize()
 
 
+# Points of the chunk-copy counter passes, in launch order: (operands, stages,
+# tiles per workgroup). "workload" is the 2^26-chunk instance; "pred_all_true"
+# is the same instance with every pred set, so no destination line is left
+# partly written.
+CHUNK_COUNTER_POINTS = [("workload", 2, 0), ("workload", 3, 0), ("workload", 2, 2),
+                        ("workload", 2, 64), ("pred_all_true", 2, 0), ("pred_all_true", 2, 2)]
+
+
 def chunk_mode(args):
-    """The chunk-copy workload at 2 stages with the default run of 64 tiles and
-    with runs of 2, `steps` times each, then the runtime's 1 GiB copy (the
-    traffic counters' calibration)."""
+    """The chunk-copy points of CHUNK_COUNTER_POINTS, `steps` launches each after
+    one untimed launch, in that order (a counter pass tells them apart by
+    dispatch order: no other chunk-copy launch happens in this mode), then the
+    runtime's 1 GiB copy three times (the traffic counters' calibration)."""
     import torch
     import software_pipelining_amd as tp
     from software_pipelining_amd import workloads
@@ -475,14 +633,16 @@ def chunk_mode(args):
     src = inp.src.reshape(-1).to(dev)
     dst = inp.dst_init.reshape(-1).to(dev)
     meta = [m.to(dev) for m in (inp.pred, inp.src_size, inp.ignore_src)]
-    gpu_warmup(lambda: tp.chunk_copy(src, dst, *meta, stages=2))
-    for tpb in (0, 2):
-        per, _ = time_launches(lambda: tp.chunk_copy(src, dst, *meta, stages=2, tiles_per_block=tpb),
-                               1, args.steps)
-        log(f"chunk copy S2 T{tpb or 64}: {median(per) * 1e3:.1f} us, "
-            f"{alg / (median(per) * 1e-3) / 1e9:.0f} GB/s on {alg} algorithmic bytes")
+    ones = torch.ones(nc, dtype=torch.uint8, device=dev)
     flat = torch.empty(1 << 28, device=dev)
     out = torch.empty_like(flat)
+    gpu_warmup(lambda: out.copy_(flat))          # clocks up, no chunk-copy dispatch
+    for operands, stages, tpb in CHUNK_COUNTER_POINTS:
+        m = meta if operands == "workload" else [ones, meta[1], meta[2]]
+        f = lambda: tp.chunk_copy(src, dst, *m, stages=stages, tiles_per_block=tpb)
+        per, _ = time_launches(f, 1, args.steps)
+        log(f"chunk copy {operands} S{stages} T{tpb}: {median(per) * 1e3:.1f} us, "
+            f"{alg / (median(per) * 1e-3) / 1e9:.0f} GB/s on the workload's {alg} algorithmic bytes")
     for _ in range(3):
         out.copy_(flat)
     torch.cuda.synchronize()
@@ -525,6 +685,9 @@ def main():
     args = parse()
     if args.record_traffic:
         record_traffic(*args.record_traffic)
+        return
+    if args.record_chunk_traffic:
+        record_chunk_traffic(*args.record_chunk_traffic)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the hot path needs no cross-GPU step and this "
@@ -835,11 +998,7 @@ def extra_rows(args, tp, workloads, torch, np, dev, x_host, xbuf, y):
     rows["map_2d"] = map_2d_row(tp, workloads, torch, np, dev, y)
 
     # predicated chunk copy: 2^26 chunks
-    if CHUNK_COPY_TIMED:
-        rows["chunk_copy"] = chunk_copy_row(tp, workloads, torch, np, dev)
-    else:
-        rows["chunk_copy"] = {"n_chunks": 1 << 26,
-                              "status": "not run: kept off the GPU until its fault fix is tested"}
+    rows["chunk_copy"] = chunk_copy_row(tp, workloads, torch, np, dev, args.cpu_seconds)
 
     # row exchange 64x4 (launch-bound)
     a = workloads.arange_rows(64).to(dev)

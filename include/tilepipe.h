@@ -262,8 +262,19 @@ TP_API int tp_map_2d(const float *src, int64_t src_stride, float *dst, int64_t d
  * alignment selects the fast path). pred, src_size, ignore_src: device arrays
  * of n_chunks bytes (any alignment), or NULL for "all 1", "all 16" and "all 0".
  * The whole 16-byte source chunk must be readable memory whatever the operands
- * say (the paragraph's bounds-check sentence); the kernel may read it. stages:
- * 1..8. tiles_per_block (256-chunk tiles): 1..65536, or 0 for the default 64.
+ * say (the paragraph's bounds-check sentence); the kernel may read it (the
+ * 16-byte load path skips a chunk whose bytes would all be dropped, the word
+ * path reads every chunk). stages: 1..8.
+ * tiles_per_block (256-chunk tiles): 1..65536, or 0 for the default of
+ * max(stages - 1, 1) tiles, so that the ring's prologue holds the whole run
+ * (on MI355X the masked writes that false preds leave are served fastest when
+ * a wave's loads come as one burst before its stores; runs of 64 tiles ran
+ * about 1.45x slower). The ring is cut to what the run can use: at most
+ * tiles_per_block + 1 slots, and one slot for runs of one tile (the same
+ * instructions in less LDS); the plan reports the stages that run. Each
+ * workgroup of 256 lanes moves one chunk per lane per tile; a 16-byte
+ * destination takes one 16-byte store per chunk, otherwise each store
+ * instruction writes 64 consecutive words of the wave's chunks.
  * dst == src is allowed; dst overlapping a metadata array is TP_ERR_OVERLAP.
  */
 TP_API int tp_chunk_copy(const void *src, void *dst, int64_t n_chunks,
@@ -279,7 +290,9 @@ TP_API int tp_chunk_copy(const void *src, void *dst, int64_t n_chunks,
  * min(src_size[i], chunk_bytes) bytes are copied and the rest of the chunk is
  * zeroed. src and dst hold n_chunks x chunk_bytes bytes, 4-byte aligned; 4-
  * and 8-byte chunks always move as 4-byte words (path_out TP_PATH_SCALAR).
- * Other chunk_bytes: TP_ERR_INVALID_ARG.
+ * Their tiles are smaller (2 and 1 KiB), so the default run is longer:
+ * max(stages - 1, 2) tiles of 8-byte and max(stages - 1, 8) tiles of 4-byte
+ * chunks. Other chunk_bytes: TP_ERR_INVALID_ARG.
  */
 TP_API int tp_chunk_copy_ex(const void *src, void *dst, int64_t n_chunks, int chunk_bytes,
                             const uint8_t *pred, const uint8_t *src_size,

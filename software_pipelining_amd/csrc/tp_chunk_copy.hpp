@@ -20,15 +20,24 @@
 //   source), or else W/4 4-byte loads covering the wave's 64 * W bytes, word
 //   after word, so every chunk lands contiguously at LDS byte tid * W
 // and on consumption reads its chunk and the three bytes back from LDS,
-// zeroes the bytes past the prefix and stores W bytes (one 16-byte store or
-// W/4 words), with
-// the store's offset out of range when pred is false, so the destination is
-// never written there. Everything a lane reads from LDS was loaded by its own
-// wave, so the per-wave vmcnt wait is the whole synchronization; no workgroup
-// barrier is needed.
+// zeroes the bytes past the prefix and stores W bytes, with the store's
+// offset out of range when pred is false, so the destination is never
+// written there. A 16-byte store writes the lane's chunk whole. Word stores
+// (8-byte chunks, or a destination that is not 16-byte aligned) are laid out
+// across the wave instead: each lane writes its masked chunk back over its own
+// LDS bytes, and store q then writes word q * 64 + lane of the wave's
+// 64 * W / 4 words, so every store instruction covers whole 64-byte blocks
+// except where pred is false (a lane storing its own chunk's words would
+// leave every instruction's blocks partly written, and the memory side serves
+// such masked writes much more slowly). Everything a lane reads from LDS was
+// loaded or written by its own wave, so the per-wave vmcnt wait is the whole
+// synchronization; no workgroup barrier is needed.
 //
-// Schedule (S data slots, 2S-1 metadata slots): a tile's metadata is loaded
-// S-1 iterations before its data, in the same issue group as the data of an
+// Schedule (S data slots, 2S-1 metadata slots). A run of at most S-1 tiles
+// fits the prologue: the metadata of every tile of the run, a wait, the data
+// of every tile, a wait, then every tile is consumed; nothing is issued past
+// the run. A longer run is pipelined: a tile's metadata is loaded S-1
+// iterations before its data, in the same issue group as the data of an
 // earlier tile. Because loads retire in order, the wait for tile t's data
 // also guarantees that the metadata of tile t+S-1, needed to mask that tile's
 // data load in the same iteration, has landed.
@@ -123,12 +132,13 @@ TP_HD __forceinline__ void chunk_copy_body(const E &e, const ChunkParams &p)
 
     auto consume = [&](uint32_t j, uint32_t dslot, uint32_t mslot) TP_INLINE {
         const Meta m = read_meta(mslot);
+        const uint32_t slot = data_ring + dslot * kData;
         u32x4 v;
         if constexpr (W == 16) {
-            v = e.template lds_load<u32x4>(data_ring + dslot * kData + tid * 16);
+            v = e.template lds_load<u32x4>(slot + tid * 16);
         } else {
             static_for<0, WPC>([&](auto w) TP_INLINE {
-                v[(int)w] = e.template lds_load<uint32_t>(data_ring + dslot * kData + tid * W + w * 4);
+                v[(int)w] = e.template lds_load<uint32_t>(slot + tid * W + w * 4);
             });
         }
         // keep bytes [0, keep): word w keeps min(max(keep - 4w, 0), 4) bytes
@@ -141,8 +151,28 @@ TP_HD __forceinline__ void chunk_copy_body(const E &e, const ChunkParams &p)
         const uint32_t off = j * kData + tid * W;
         if constexpr (SX4) {
             e.store_b128(rdst, m.store ? off : run_end, v);
+        } else if constexpr (WPC == 1) {
+            e.store_b32(rdst, m.store ? off : run_end, v[0]);
         } else {
-            static_for<0, WPC>([&](auto w) TP_INLINE { e.store_b32(rdst, m.store ? off + w * 4 : run_end, v[(int)w]); });
+            // the masked chunk back over the lane's own bytes, then the
+            // wave's words in order: word q * 64 + lane belongs to the wave's
+            // chunk (q * 64 + lane) / WPC, whose pred decides the store
+            if constexpr (W == 16) {
+                e.template lds_store<u32x4>(slot + tid * 16, v);
+            } else {
+                static_for<0, WPC>([&](auto w) TP_INLINE {
+                    e.template lds_store<uint32_t>(slot + tid * W + w * 4, v[(int)w]);
+                });
+            }
+            const uint32_t wave_bytes = wave_first * W;   // the wave's chunks in the slot and in dst
+            const uint32_t meta = meta_ring + mslot * kMeta + meta_wave;
+            static_for<0, WPC>([&](auto q) TP_INLINE {
+                const uint32_t wi = q * 64 + lane;
+                const bool st = has_pred ? e.template lds_load<uint8_t>(meta + wi / WPC * 4) != 0
+                                         : true;
+                const uint32_t word = e.template lds_load<uint32_t>(slot + wave_bytes + wi * 4);
+                e.store_b32(rdst, st ? j * kData + wave_bytes + wi * 4 : run_end, word);
+            });
         }
     };
 
@@ -154,6 +184,22 @@ TP_HD __forceinline__ void chunk_copy_body(const E &e, const ChunkParams &p)
             e.template wait<0>();
             consume(t, 0, 0);
         }
+    } else if (cnt <= S - 1) {
+        // the whole run in the prologue: nothing is issued past its last tile
+        static_for<0, S - 1>([&](auto m) TP_INLINE {
+            if ((int)m < cnt)
+                issue_meta(m, m);
+        });
+        e.template wait<0>();
+        static_for<0, S - 1>([&](auto g) TP_INLINE {
+            if ((int)g < cnt)
+                issue_data(g, g, g);
+        });
+        e.template wait<0>();
+        static_for<0, S - 1>([&](auto g) TP_INLINE {
+            if ((int)g < cnt)
+                consume(g, g, g);
+        });
     } else {
         static_for<0, S - 1>([&](auto m) TP_INLINE { issue_meta(m, m); });
         e.template wait<0>();

@@ -201,6 +201,13 @@ struct GpuEngine {
     {
         return *reinterpret_cast<const T *>(lds + off);
     }
+    // A wave's own write into LDS (ds_write). LDS operations of one wave
+    // execute in order, so the wave's later reads of these bytes see them.
+    template <class T>
+    __device__ __forceinline__ void lds_store(uint32_t off, T v) const
+    {
+        *reinterpret_cast<T *>(lds + off) = v;
+    }
     __device__ __forceinline__ BufferRes res(const void *base, uint32_t num_records) const
     {
         return make_buffer_res(base, num_records);

@@ -16,7 +16,6 @@ namespace tp {
 
 constexpr int kMaxStages = 8;
 constexpr int kDefaultMapTilesPerBlock = 2;     // pipelined map, tiles_per_block == 0
-constexpr int kDefaultChunkTilesPerBlock = 64;  // chunk copy, tiles_per_block == 0
 constexpr int kMaxTilesPerBlock = 65536;
 constexpr int kMaxRowShiftRows = 1024;
 constexpr int kChunkTile = 256;            // chunks per tile of the chunk copy (one per lane)

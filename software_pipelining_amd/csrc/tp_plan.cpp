@@ -304,11 +304,29 @@ int plan_chunk_copy(uintptr_t src, uintptr_t dst, int64_t n_chunks, int chunk_by
         return TP_ERR_INVALID_ARG;
     if (stages < 1 || stages > kMaxStages)
         return TP_ERR_INVALID_ARG;
-    const int tpb = resolve_tiles_per_block(tiles_per_block, kDefaultChunkTilesPerBlock);
+    // The default run is max(S-1, m) tiles. With S-1 tiles the prologue puts
+    // the whole run in flight: every metadata load, then every data load,
+    // then the stores. For 16-byte chunks under the masked writes that a false
+    // pred leaves this measured fastest on MI355X at every stage count (runs
+    // of 64 tiles ran about 1.45x slower). Narrower chunks make smaller tiles
+    // (2 and 1 KiB) whose per-workgroup metadata round trip needs longer runs
+    // to amortize: m = 1, 2 and 8 tiles for 16-, 8- and 4-byte chunks
+    // (measured best, or within a few percent of it, at 1-6 stages).
+    const int min_run = chunk_bytes == 16 ? 1 : chunk_bytes == 8 ? 2 : 8;
+    const int tpb = resolve_tiles_per_block(tiles_per_block,
+                                            stages - 1 > min_run ? stages - 1 : min_run);
     if (tpb < 0)
         return TP_ERR_INVALID_ARG;
     if ((int64_t)tpb * chunk_data_slot_bytes(chunk_bytes) > kMaxRunBytes)
         return TP_ERR_INVALID_ARG;
+    // A ring deeper than the run plus one slot holds nothing more (the
+    // prologue already issues the whole run), and a run of one tile moves with
+    // the same instructions on the one-stage schedule: the ring is cut to what
+    // the run can use, which only frees LDS.
+    if (tpb == 1)
+        stages = 1;
+    else if (stages > tpb + 1)
+        stages = tpb + 1;
     tp_plan p;
     memset(&p, 0, sizeof p);
     p.stages = stages;

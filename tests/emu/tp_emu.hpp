@@ -97,22 +97,22 @@ struct Res {
     uint32_t num_records;
 };
 
-enum Kind { K_NONE, K_UNIFORM, K_LDS_LOAD, K_DMA, K_STORE, K_WAIT, K_BARRIER, K_DONE };
+enum Kind { K_NONE, K_UNIFORM, K_LDS_LOAD, K_DMA, K_STORE, K_WAIT, K_BARRIER, K_DONE, K_LDS_STORE };
 
 inline const char *kind_name(int k)
 {
     static const char *n[] = {"none", "readfirstlane", "LDS read", "LDS-DMA load", "store",
-                              "vmcnt wait", "barrier", "end"};
+                              "vmcnt wait", "barrier", "end", "LDS write"};
     return n[k];
 }
 
 struct Request {
     int kind = K_NONE;
-    uint32_t a = 0, b = 0;   // UNIFORM: a = value; LDS_LOAD: a = offset, b = size;
+    uint32_t a = 0, b = 0;   // UNIFORM: a = value; LDS_LOAD, LDS_STORE: a = offset, b = size;
                              // DMA: a = voff, b = m0; STORE: a = voff; WAIT: a = K
     int width = 0;           // DMA/STORE: 16, 4 or 1 bytes
     Res res{};
-    uint8_t data[16];        // STORE data, LDS_LOAD result
+    uint8_t data[16];        // STORE and LDS_STORE data, LDS_LOAD result
     uint32_t result = 0;     // UNIFORM result
 };
 
@@ -138,8 +138,8 @@ struct VmOp {
 
 struct Shadow {
     int64_t pending = -1;    // id of the in-flight load that writes this byte
-    int16_t writer = -1;     // wave of the last load that wrote it (-1: never written)
-    int64_t write_epoch = 0; // barrier epoch in which that load retired
+    int16_t writer = -1;     // wave of the last load or LDS write that wrote it (-1: never)
+    int64_t write_epoch = 0; // barrier epoch in which that load retired (or the write ran)
     uint32_t readers = 0;    // waves that read it in epoch read_epoch (bit mask)
     int64_t read_epoch = -1;
 };
@@ -305,6 +305,7 @@ class Emulator {
             break;
         }
         case K_LDS_LOAD: lds_read(w); break;
+        case K_LDS_STORE: lds_write(w); break;
         case K_DMA: dma(w); break;
         case K_STORE: store(w); break;
         case K_WAIT: {
@@ -357,6 +358,35 @@ class Emulator {
                 s.readers |= 1u << w.id;
             }
             memcpy(l->req.data, lds.data() + off, n);
+        }
+    }
+
+    // A wave's own LDS write: it lands at once (LDS operations of a wave run in
+    // order). The bytes must not be the target of a load still in flight, nor
+    // have been read or written by another wave since the last barrier.
+    void lds_write(Wave &w)
+    {
+        for (Lane *l : w.lanes) {
+            const uint32_t off = l->req.a, n = l->req.b;
+            if ((uint64_t)off + n > lds_bytes)
+                fail("workgroup %u wave %d lane %u: LDS write of %u bytes at %u, outside the "
+                     "%u-byte allocation", block, w.id, l->tid, n, off, lds_bytes);
+            for (uint32_t i = 0; i < n; ++i) {
+                Shadow &s = shadow[off + i];
+                if (s.pending >= 0)
+                    fail("workgroup %u wave %d lane %u: LDS write to byte %u while a load that "
+                         "writes it is still in flight", block, w.id, l->tid, off + i);
+                if (s.read_epoch == epoch && (s.readers & ~(1u << w.id)))
+                    fail("workgroup %u wave %d lane %u: LDS write to byte %u, which another "
+                         "wave read with no barrier in between", block, w.id, l->tid, off + i);
+                if (s.writer >= 0 && s.writer != w.id && s.write_epoch >= epoch)
+                    fail("workgroup %u wave %d lane %u: LDS write to byte %u, which wave %d "
+                         "wrote with no barrier in between", block, w.id, l->tid, off + i,
+                         s.writer);
+                s.writer = (int16_t)w.id;
+                s.write_epoch = epoch;
+            }
+            memcpy(lds.data() + off, l->req.data, n);
         }
     }
 
@@ -503,6 +533,17 @@ struct EmuEngine {
         T v;
         memcpy(&v, g_lane->req.data, sizeof(T));
         return v;
+    }
+    template <class T>
+    void lds_store(uint32_t off, T v) const
+    {
+        static_assert(sizeof(T) <= 16, "LDS writes of at most 16 bytes");
+        Request r;
+        r.kind = K_LDS_STORE;
+        r.a = off;
+        r.b = sizeof(T);
+        memcpy(r.data, &v, sizeof(T));
+        g_emu->post(r);
     }
     Res res(const void *base, uint32_t num_records) const
     {

@@ -5,15 +5,6 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-# The chunk-copy kernel made two GPU memory faults before its cause was found:
-# the compiler rebuilt buffer descriptors with v_readfirstlane right before the
-# inline-asm buffer instructions, which then read stale SGPRs (a VALU-written
-# SGPR needs 5 wait states before a vector-memory instruction reads it). The
-# asm blocks now carry those wait states and a static check of the built code
-# object enforces them (test_isa_hazards.py); its kernel source also runs under
-# the CPU emulator (tests/test_emu_chunk_copy.py). None means the GPU tests run.
-CHUNK_COPY_GPU_SKIP = None
-
 GUARD = 64                      # sentinel words before and after every buffer
 SENTINEL = 0x7FC0DEAD           # a NaN pattern none of the tests' results contain
 

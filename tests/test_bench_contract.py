@@ -106,3 +106,41 @@ def test_record_traffic_scales_by_the_copy(tmp_path):
         e = json.load(f)[key]
     assert e["scale"] == {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
     assert e["kernel_source_hash"] == bench.kernel_source_hash()
+
+
+def test_record_chunk_traffic_groups_dispatches_by_order(tmp_path):
+    # the chunk-copy dispatches of `--mode chunk` fall in one group per point
+    # of CHUNK_COUNTER_POINTS (one untimed launch, then the timed ones): each
+    # point's bytes are the median of its timed launches, calibrated on the
+    # runtime's 1 GiB copy, and the entry is tied to the chunk copy's sources
+    import csv
+    import json
+    bench = _bench()
+    pts = bench.CHUNK_COUNTER_POINTS
+    for counter, sub, copy_kib in (("FETCH_SIZE", "f", 524288.0), ("WRITE_SIZE", "w", 1048576.0)):
+        path = tmp_path / sub / "x_counter_collection.csv"
+        os.makedirs(path.parent, exist_ok=True)
+        with open(path, "w", newline="") as f:
+            w = csv.writer(f)
+            w.writerow(["Dispatch_Id", "Grid_Size", "Kernel_Name", "Counter_Name", "Counter_Value"])
+            did = 0
+            for i, _ in enumerate(pts):
+                for j in range(4):          # untimed launch (a stray value), then 3 timed
+                    val = 9e9 if j == 0 else 1000.0 * (i + 1) + j
+                    w.writerow([did, 1 << 18, "void tp::dev::chunk_copy_kernel<1, 16, true, true>",
+                                counter, val])
+                    did += 1
+            w.writerow([did, 1 << 25, "__amd_rocclr_copyBuffer", counter, copy_kib])
+    out = str(tmp_path / "traffic.json")
+    bench.record_chunk_traffic(str(tmp_path / "f"), str(tmp_path / "w"), out)
+    with open(out) as f:
+        table = json.load(f)
+    for i, (operands, stages, tpb) in enumerate(pts):
+        plan = tp.plan_chunk_copy(1 << 40, 1 << 41, 1 << 26, stages=stages, tiles_per_block=tpb)
+        e = table[bench.chunk_traffic_key(operands, plan.stages, plan.tiles_per_block)]
+        mid = 1000.0 * (i + 1) + 2          # median of the three timed launches
+        assert e["fetch_bytes"] == round(mid * 2 * 1024) and e["write_bytes"] == round(mid * 1024)
+        assert e["kernel_source_hash"] == bench.kernel_source_hash(bench.CHUNK_KERNEL_SOURCES)
+    assert len({bench.chunk_traffic_key(o, *(lambda p: (p.stages, p.tiles_per_block))(
+        tp.plan_chunk_copy(1 << 40, 1 << 41, 1 << 26, stages=s, tiles_per_block=t)))
+        for o, s, t in pts}) == len(pts)

@@ -138,21 +138,22 @@ def test_narrow_chunks(width):
             assert np.array_equal(dst, expected), (width, stages, src_off, dst_off)
 
 
-@pytest.mark.parametrize("stages,tpb", [(1, 0), (2, 0), (4, 0), (2, 1), (2, 2), (2, 8)])
+@pytest.mark.parametrize("stages,tpb", [(1, 0), (2, 0), (3, 0), (4, 0), (2, 2), (2, 8), (2, 64)])
 def test_full_size_boundary_workgroups(stages, tpb):
-    # the chunk-copy workload's launches (2^26 chunks; the default 64 tiles per
-    # workgroup, 4096 workgroups, and runs of 1, 2 and 8 tiles): the first, a
-    # middle and the last workgroup run on buffers of the full size (pages
-    # that are never touched are never allocated); only their ranges hold data
+    # the chunk-copy workload's launches (2^26 chunks; the default runs of
+    # max(1, S-1) tiles, and runs of 2, 8 and 64 tiles): the first, a middle
+    # and the last workgroup run on buffers of the full size (pages that are
+    # never touched are never allocated); only their ranges hold data
     n = 1 << 26
-    per_block = (tpb or 64) * 256
-    grid = n // per_block
+    run = tpb or max(1, stages - 1)
+    per_block = run * 256
+    grid = -(-n // per_block)                  # a run of 3 tiles leaves a short last run
     blocks = [0, grid // 2 - 1, grid - 1]
     rng = np.random.default_rng(5)
     src = np.zeros(n * 16, np.uint8)
     pred, size, ign = (np.zeros(n, np.uint8) for _ in range(3))
     for b in blocks:
-        lo, hi = b * per_block, (b + 1) * per_block
+        lo, hi = b * per_block, min(n, (b + 1) * per_block)
         src[16 * lo:16 * hi] = rng.integers(0, 256, 16 * (hi - lo), dtype=np.uint8)
         pred[lo:hi] = rng.random(hi - lo) < 0.9
         size[lo:hi] = rng.choice(np.array([0, 4, 8, 12, 16], np.uint8), hi - lo)
@@ -160,13 +161,15 @@ def test_full_size_boundary_workgroups(stages, tpb):
     fill = np.frombuffer(np.full(4 * per_block, DEADBEEF, np.uint32).tobytes(), np.uint8)
     dst = np.zeros(n * 16, np.uint8)
     for b in blocks:
-        dst[16 * b * per_block:16 * (b + 1) * per_block] = fill
+        lo, hi = b * per_block, min(n, (b + 1) * per_block)
+        dst[16 * lo:16 * hi] = fill[:16 * (hi - lo)]
     plan = emu.chunk_copy(src, dst, pred, size, ign, stages=stages, tiles_per_block=tpb,
                           blocks=blocks, policy=stages % 4)
-    assert plan.grid == grid and plan.tiles_per_block == (tpb or 64)
+    assert plan.grid == grid and plan.tiles_per_block == run
     for b in blocks:
-        lo, hi = b * per_block, (b + 1) * per_block
-        exp = oracle.chunk_copy(src[16 * lo:16 * hi], fill, pred[lo:hi], size[lo:hi], ign[lo:hi])
+        lo, hi = b * per_block, min(n, (b + 1) * per_block)
+        exp = oracle.chunk_copy(src[16 * lo:16 * hi], fill[:16 * (hi - lo)], pred[lo:hi],
+                                size[lo:hi], ign[lo:hi])
         assert np.array_equal(dst[16 * lo:16 * hi], exp), (stages, tpb, b)
 
 

@@ -11,10 +11,9 @@ import torch
 import oracle
 import software_pipelining_amd as tp
 from software_pipelining_amd import workloads
-from tests.gpu_util import CHUNK_COPY_GPU_SKIP, Guarded, assert_bits_equal, to_device
+from tests.gpu_util import Guarded, assert_bits_equal, to_device
 
-pytestmark = [pytest.mark.gpu,
-              pytest.mark.skipif(CHUNK_COPY_GPU_SKIP is not None, reason=str(CHUNK_COPY_GPU_SKIP))]
+pytestmark = pytest.mark.gpu
 
 DEADBEEF = 0xDEADBEEF
 

@@ -16,7 +16,7 @@ import torch
 import oracle
 import software_pipelining_amd as tp
 from software_pipelining_amd import workloads
-from tests.gpu_util import CHUNK_COPY_GPU_SKIP, assert_equal_on_device
+from tests.gpu_util import assert_equal_on_device
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -65,7 +65,6 @@ def test_config3_stage_tile_sweep(cuda_device):
         del exp
 
 
-@pytest.mark.skipif(CHUNK_COPY_GPU_SKIP is not None, reason=str(CHUNK_COPY_GPU_SKIP))
 def test_config4_predicated_chunk_copy(cuda_device):
     nc = 1 << 26
     inp = workloads.chunk_copy_inputs(nc, seed=3)
@@ -74,9 +73,9 @@ def test_config4_predicated_chunk_copy(cuda_device):
     exp_d = torch.from_numpy(exp.reshape(-1)).to(cuda_device)
     src = inp.src.reshape(-1).to(cuda_device)
     meta = [m.to(cuda_device) for m in (inp.pred, inp.src_size, inp.ignore_src)]
-    # the launches the benchmark times: the default run of 64 tiles at 1, 2 and
-    # 4 stages, and runs of 1, 2 and 8 tiles at 2 stages
-    for stages, tpb in ((1, 0), (2, 0), (4, 0), (2, 1), (2, 2), (2, 8)):
+    # the launches the benchmark times: the default runs (max(1, S-1) tiles) at
+    # 1-4 stages, and runs of 2, 8 and 64 tiles at 2 stages
+    for stages, tpb in ((1, 0), (2, 0), (3, 0), (4, 0), (2, 2), (2, 8), (2, 64)):
         dst = inp.dst_init.reshape(-1).to(cuda_device)
         print(f"config 4 chunk_copy n=2^26 S={stages} T={tpb}", flush=True)
         tp.chunk_copy(src, dst, *meta, stages=stages, tiles_per_block=tpb)

@@ -66,8 +66,12 @@ def test_map_plan_default_run_length():
     assert p.tiles_per_block == 2 and p.grid == (1 << 20) // 2
     p = tp.plan_map(A, B, 5000, "scale2", 1024, 2, 0)
     assert (p.num_tiles, p.grid) == (5, 3)
-    p = tp.plan_chunk_copy(A, B, 1 << 26)
-    assert p.tiles_per_block == 64
+    # the chunk copy's default run is max(S-1, m) tiles, m = 1, 2, 8 for 16-,
+    # 8- and 4-byte chunks: with 16-byte chunks the prologue holds the whole run
+    for width, stages, run in ((16, 1, 1), (16, 2, 1), (16, 3, 2), (16, 4, 3), (16, 8, 7),
+                               (8, 1, 2), (8, 2, 2), (8, 4, 3), (4, 2, 8), (4, 8, 8)):
+        p = tp.plan_chunk_copy(A, B, 1 << 26, stages=stages, chunk_bytes=width)
+        assert p.tiles_per_block == run, (width, stages)
 
 
 def test_map_plan_tail_and_small_sizes():
@@ -414,15 +418,33 @@ def test_row_shift_plan():
 
 # ----------------------------------------------------------- chunk copy
 def test_chunk_copy_plan():
-    p = tp.plan_chunk_copy(A, B, 1 << 26)
+    p = tp.plan_chunk_copy(A, B, 1 << 26, stages=2, tiles_per_block=64)
     assert (p.threads, p.tile_units, p.num_tiles, p.grid) == (256, 256, 1 << 18, 1 << 12)
     assert p.lds_bytes == 2 * 4096 + 3 * 3072
     assert p.wait_steady == 0 * 4 + 1 * 1
+    # default: runs of one tile on the one-stage schedule
+    p = tp.plan_chunk_copy(A, B, 1 << 26)
+    assert (p.stages, p.tiles_per_block, p.grid, p.wait_steady) == (1, 1, 1 << 18, 0)
+    assert p.lds_bytes == 4096 + 3072
     assert tp.plan_chunk_copy(A, B, 10, stages=4).wait_steady == 2 * 4 + 3 * 1
     assert tp.plan_chunk_copy(A + 4, B + 4, 10, stages=3).wait_steady == 1 * 7 + 2 * 4
     assert tp.plan_chunk_copy(A + 4, B, 10).path == tp.Path.SCALAR_LOAD
     assert tp.plan_chunk_copy(A, A, 10).grid == 1
     assert tp.plan_chunk_copy(0, 0, 0).grid == 0
+
+
+def test_chunk_copy_ring_cut_to_the_run():
+    # more slots than the run plus one hold nothing: the ring is cut to
+    # tiles_per_block + 1 slots, and a run of one tile takes the one-stage
+    # schedule (the same instructions in less LDS)
+    for stages, tpb, eff in ((8, 2, 3), (8, 1, 1), (2, 1, 1), (4, 3, 4), (2, 5, 2), (5, 64, 5),
+                             (3, 2, 3), (1, 7, 1)):
+        p = tp.plan_chunk_copy(A, B, 100000, stages=stages, tiles_per_block=tpb)
+        assert (p.stages, p.tiles_per_block) == (eff, tpb), (stages, tpb)
+        assert p.lds_bytes == eff * 4096 + (2 * eff - 1) * 3072
+    # the LDS budget is checked on the ring that runs
+    assert tp.plan_chunk_copy(A, B, 10, stages=8, tiles_per_block=1,
+                              lds_budget=8 * 1024).stages == 1
 
 
 def test_chunk_copy_plan_errors():
@@ -446,7 +468,7 @@ def test_chunk_copy_widths_plan():
         assert p.path == (tp.Path.X4 if w == 16 else tp.Path.SCALAR)
         assert p.ring_bytes == 3 * 256 * w + 5 * 3 * 256 * 4
         assert p.wait_steady == 1 * (3 + ld) + 2 * st                      # (S-2) ld + (S-1) st
-        assert (p.num_tiles, p.grid) == (4, 1)
+        assert (p.num_tiles, p.grid) == (4, 1 if w == 4 else 2)   # default runs 2, 2, 8
     assert tp.plan_chunk_copy(A + 4, B + 4, 10, chunk_bytes=8).path == tp.Path.SCALAR
     assert tp.plan_chunk_copy(A, B, 10).chunk_bytes == 16
     for bad in (0, 2, 12, 32):
