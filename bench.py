@@ -340,27 +340,45 @@ def cpu_baseline(x_host, op, bytes_per_elem, seconds):
                       f"{sum(times):.1f} s, median pass {t * 1e3:.1f} ms"}
 
 
+# Points of the stage counter passes, in launch order: (op, tiles per
+# workgroup, bound on resident workgroups per CU, stages), all at tile 1024.
+# horner32 at the library's launch (runs of 2, no bound: it fills every wave
+# slot), then both ops at 16 tiles per workgroup with no bound (8 workgroups
+# per CU, wave-limited), then horner32 at 8 tiles per workgroup and 2
+# workgroups per CU (8 waves per CU), then scale2 at the library's launch.
+STAGE_COUNTER_POINTS = ([("horner32", 0, 0, S) for S in (1, 2, 4)]
+                        + [(op, 16, -1, S) for op in ("horner32", "scale2") for S in (1, 2, 3, 4)]
+                        + [("horner32", 8, 2, S) for S in (1, 2, 3, 4)]
+                        + [("scale2", 0, 0, S) for S in (1, 2, 4)])
+
+
 def stages_mode(args):
-    """Launch the maps at stages 1..4 with a fixed grid and occupancy, a few
-    times each, for per-stage counter passes: tile 1024 with 16 tiles per
-    workgroup and no bound on resident workgroups (8 per CU, wave-limited),
-    and horner32 also with 8 tiles per workgroup at 2 workgroups per CU."""
+    """Each point of STAGE_COUNTER_POINTS `steps` times after one untimed
+    launch, in that order (a counter pass tells the points apart by dispatch
+    order: no other map launch happens in this mode), then the runtime's
+    1 GiB copy three times (the traffic counters' calibration)."""
     import torch
     import software_pipelining_amd as tp
     from software_pipelining_amd import workloads
     dev = torch.device("cuda:0")
-    for op, n, seed, runs in (("horner32", 1 << 27, 4, ((16, -1), (8, 2))),
-                              ("scale2", 1 << 28, 2, ((16, -1),))):
-        x = workloads.uniform_pm1(n, seed=seed).to(dev)
-        y = torch.empty_like(x)
-        gpu_warmup(lambda: tp.pipelined_map(x, y, op, 1024, 2, 16, resident_cap=-1))
-        for tpb, cap in runs:
-            for S in (1, 2, 3, 4):
-                f = lambda: tp.pipelined_map(x, y, op, 1024, S, tpb, resident_cap=cap)
-                per, _ = time_launches(f, 2, args.steps)
-                occ = "8 WG/CU" if cap < 0 else f"{cap} WG/CU"
-                log(f"{op} tile 1024 T{tpb} {occ} S{S}: {median(per) * 1e3:.1f} us")
-        del x, y
+    xs = {"horner32": workloads.uniform_pm1(1 << 27, seed=4).to(dev),
+          "scale2": workloads.uniform_pm1(1 << 28, seed=2).to(dev)}
+    ys = {op: torch.empty_like(x) for op, x in xs.items()}
+    flat = torch.empty(1 << 28, device=dev)
+    # Clocks up under the compute-heavy load the first points run (after a
+    # memory-bound warm-up the first horner32 launches ran up to 15 % slower),
+    # with the role-split kernel, which is not a map_kernel dispatch.
+    gpu_warmup(lambda: tp.pipelined_map(xs["horner32"], ys["horner32"], "horner32", 1024, 2, 0,
+                                        schedule="role_split"), 300)
+    for op, tpb, cap, S in STAGE_COUNTER_POINTS:
+        x, y = xs[op], ys[op]
+        f = lambda: tp.pipelined_map(x, y, op, 1024, S, tpb, resident_cap=cap)
+        per, _ = time_launches(f, 1, args.steps)
+        occ = {0: "library", -1: "8 WG/CU"}.get(cap, f"{cap} WG/CU")
+        log(f"{op} tile 1024 T{tpb or 'default'} {occ} S{S}: {median(per) * 1e3:.1f} us")
+    out = torch.empty_like(flat)
+    for _ in range(3):                           # the traffic counters' calibration
+        out.copy_(flat)
     torch.cuda.synchronize()
 
 
