@@ -42,7 +42,7 @@ def parse():
                     help="consecutive tiles per workgroup (0: the library default)")
     ap.add_argument("--quick", action="store_true", help="headline only: no sweep, no extra rows")
     ap.add_argument("--mode", choices=("bench", "stages", "sweep", "occupancy", "map2d", "align",
-                                       "strides", "chunk"),
+                                       "strides", "chunk", "misaligned"),
                     default="bench",
                     help="stages: only the maps at 1-4 stages; sweep: only the 36-point stage/tile "
                          "sweep (both for hardware-counter passes); occupancy: scale2 bandwidth "
@@ -52,7 +52,10 @@ def parse():
                          "strides: 2-D map bandwidth against the source's row padding and the "
                          "run width; chunk: only the chunk copy (the points of "
                          "CHUNK_COUNTER_POINTS, in order) and the runtime's 1 GiB copy, for "
-                         "counter passes")
+                         "counter passes; misaligned: scale2 with the source on or 4 bytes off "
+                         "a line against the run length (MISALIGNED_POINTS)")
+    ap.add_argument("--rounds", type=int, default=1,
+                    help="interleaved rounds of --mode misaligned")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU work: read the rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE outputs "
@@ -226,7 +229,7 @@ def record_traffic(fetch_dir: str, write_dir: str, path: str | None = None):
                   "scale": {c: round(v["scale"], 5) for c, v in out.items()},
                   "counter_kib": {c: {"map": v["map_kib"], "copy_1GiB": v["copy_kib"],
                                       "map_dispatches": v["dispatches"]} for c, v in out.items()},
-                  "source": "profiles/map_scale2_2p28_t256_s2_T2_hbm_traffic.md"}
+                  "source": "profiles/map_scale2_2p28_t256_s2_T4_hbm_traffic.md"}
     with open(path, "w") as f:
         json.dump(table, f, indent=1)
         f.write("\n")
@@ -666,6 +669,45 @@ def chunk_mode(args):
     torch.cuda.synchronize()
 
 
+# Points of `--mode misaligned`, in launch order: (source offset in floats,
+# tile, tiles per workgroup), scale2 over 2^28 floats at 2 stages.
+MISALIGNED_POINTS = [(off, tile, T) for off in (0, 1) for tile in (256, 1024) for T in (2, 3, 4, 8)]
+
+
+def misaligned_mode(args):
+    """scale2 over 2^28 floats with the source on a 256-byte boundary or 4
+    bytes past it, tiles 256 and 1024, runs of 2, 3, 4 and 8 tiles, 2 stages
+    (the library's residency bound for each): `rounds` interleaved rounds of
+    one untimed and `steps` timed launches per point, in the order of
+    MISALIGNED_POINTS (with one round, a counter pass tells the points apart by
+    dispatch order), then the runtime's 1 GiB copy three times (the traffic
+    counters' calibration)."""
+    import torch
+    import software_pipelining_amd as tp
+    dev = torch.device("cuda:0")
+    n = 1 << 28
+    xb = torch.empty(n + 64, device=dev).uniform_(-1, 1)
+    y = torch.empty(n, device=dev)
+    if xb.data_ptr() % 256 or y.data_ptr() % 256:
+        raise RuntimeError("the buffers must start on a 256-byte boundary")
+    flat = torch.empty(1 << 28, device=dev)
+    out = torch.empty_like(flat)
+    gpu_warmup(lambda: out.copy_(flat))          # clocks up, no map dispatch
+    res = {p: [] for p in MISALIGNED_POINTS}
+    for _ in range(args.rounds):
+        for off, tile, T in MISALIGNED_POINTS:
+            x = xb[off:off + n]
+            per, _ = time_launches(lambda: tp.pipelined_map(x, y, "scale2", tile, 2, T), 1, args.steps)
+            res[(off, tile, T)] += per
+    for off, tile, T in MISALIGNED_POINTS:
+        us = median(res[(off, tile, T)]) * 1e3
+        log(f"misaligned source +{4 * off} B tile {tile} T{T}: {us:.1f} us, "
+            f"{8 * n / (us * 1e-6) / 1e9:.0f} GB/s")
+    for _ in range(3):
+        out.copy_(flat)
+    torch.cuda.synchronize()
+
+
 def align_mode(args):
     """scale2 over 2^28 with in and out at byte offsets from a 256-byte
     boundary, under the library's realignment and under the pages' 4-byte
@@ -732,6 +774,9 @@ def main():
         return
     if args.mode == "chunk":
         chunk_mode(args)
+        return
+    if args.mode == "misaligned":
+        misaligned_mode(args)
         return
 
     import numpy as np

@@ -163,10 +163,11 @@ TP_API int tp_row_shift(const float *a, float *b, int64_t rows, void *stream, in
  * stored. in, out: device buffers of n float32. op: tp_op.
  * tile_elems: 256, 512, 1024, 2048, 4096 or 8192. stages: 1..8 ("Typically 2-4
  * stages": the guide's FAQ; 1 = load, wait, compute, store with no overlap).
- * tiles_per_block: 1..65536, or 0 for the library default of 2 (the shortest
- * run in which one tile's load overlaps the previous tile's compute; on
- * MI355X short runs dispatched in order keep the memory traffic of all
- * resident workgroups within a narrow window and stream fastest).
+ * tiles_per_block: 1..65536, or 0 for the library default: runs of 4 tiles
+ * of at most 512 floats, of 2 larger tiles. On MI355X short runs dispatched in
+ * order keep the memory traffic of all resident workgroups within a narrow
+ * window and stream fastest; runs of 4 KiB (tile 256) to 8 KiB (tiles 512
+ * and 1024) were measured fastest, and runs of 3, 5 or 6 tiles 4-9 % slower.
  * stages * tile_elems * 4 must fit the device's LDS per workgroup
  * (TP_ERR_LDS_BUDGET). out == in is allowed. Buffers off a 128-byte boundary
  * are moved as TP_ALIGN_REALIGN describes: the floats before out's first
@@ -190,7 +191,7 @@ TP_API int tp_pipelined_map(const float *in, float *out, int64_t n, int op,
  * is in flight at once on a CU, never the result.
  *   resident_cap  0: the library's policy. For the streaming ops (scale2,
  *                    copy) with runs of 2 or more tiles of at most 1024
- *                    floats it keeps about 28 KiB x (1 + 1/T) of tile traffic
+ *                    floats it keeps about 27 KiB x (1 + 1/T) of tile traffic
  *                    per CU in flight: each resident workgroup has a(T,S) + 1
  *                    tiles moving on average (a = mean over a run of
  *                    min(S, tiles left) loads, plus the stores behind them),

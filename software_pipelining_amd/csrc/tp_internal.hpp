@@ -15,7 +15,13 @@
 namespace tp {
 
 constexpr int kMaxStages = 8;
-constexpr int kDefaultMapTilesPerBlock = 2;     // pipelined map, tiles_per_block == 0
+// Default run of the pipelined map (tiles_per_block == 0): 4 tiles of at most
+// 2 KiB, else 2. Measured on MI355X (scale2 over 2^28 floats, 2 stages):
+// tile 256 streams 1.0-1.6 % faster in runs of 4 (4 KiB) than of 2, tile 512
+// 1.4 % faster in runs of 4 (8 KiB); tile 1024 is fastest in runs of 2
+// (8 KiB) and runs of 4 lose 7 %. Runs of 3, 5 or 6 tiles lost 4-9 %.
+constexpr int default_map_run(int tile_elems) { return tile_elems * 4 <= 2048 ? 4 : 2; }
+constexpr int kDefaultMap2dBoxesPerBlock = 2;    // 2-D map, boxes_per_block == 0
 constexpr int kMaxTilesPerBlock = 65536;
 constexpr int kMaxRowShiftRows = 1024;
 constexpr int kChunkTile = 256;            // chunks per tile of the chunk copy (one per lane)
@@ -35,7 +41,7 @@ constexpr int64_t kMaxRunBytes = int64_t(1) << 30;   // bytes one workgroup stre
 constexpr int kLdsPerCu = 160 * 1024;      // gfx950: LDS of one CU, all of it usable by one workgroup
 constexpr int kMaxWavesPerCu = 32;         // gfx950: 8 wave slots on each of 4 SIMDs
 constexpr int kLdsReserveGranule = 1024;   // padding to bound residency is whole KiB
-constexpr int kInflightTargetBytes = 28 * 1024;   // streaming map: tile traffic in flight per CU
+constexpr int kInflightTargetBytes = 27 * 1024;   // streaming map: tile traffic in flight per CU
 constexpr int kMinResidentWaves = 8;       // ... but never fewer resident waves per CU
 constexpr int kMinResidentWorkgroups = 4;  // ... nor fewer resident workgroups
 

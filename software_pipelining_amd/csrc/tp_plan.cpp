@@ -64,7 +64,7 @@ int map_policy_resident_cap(int op, int tile_elems, int stages, int tiles_per_bl
 {
     // A wave of the streaming ops is almost always waiting on memory, so the
     // resident workgroups decide how much traffic is in flight; past roughly
-    // 28 KiB per CU (with headroom for the start and end of short runs) the
+    // 27 KiB per CU (with headroom for the start and end of short runs) the
     // extra requests only queue, and HBM efficiency drops. horner32 spends
     // most of a wave's time in FMAs and needs every wave to hide it; a run of
     // one tile has no pipeline and lives too briefly to be bounded; and where
@@ -131,7 +131,7 @@ int plan_map(uintptr_t in, uintptr_t out, int64_t n, int op, int tile_elems, int
         return TP_ERR_INVALID_ARG;
     if (!valid_tile(tile_elems) || stages < 1 || stages > kMaxStages)
         return TP_ERR_INVALID_ARG;
-    const int tpb = resolve_tiles_per_block(tiles_per_block, kDefaultMapTilesPerBlock);
+    const int tpb = resolve_tiles_per_block(tiles_per_block, default_map_run(tile_elems));
     if (tpb < 0)
         return TP_ERR_INVALID_ARG;
     // a workgroup's run (plus S-1 tiles of out-of-range prefetch) must stay
@@ -161,12 +161,6 @@ int plan_map(uintptr_t in, uintptr_t out, int64_t n, int op, int tile_elems, int
     }
     if (p.ring_bytes > lds_budget)
         return TP_ERR_LDS_BUDGET;
-    const int waves = p.threads / 64;
-    const int cap = resident_cap == 0 ? map_policy_resident_cap(op, tile_elems, stages, tpb, waves)
-                                      : resident_cap;
-    p.resident_cap = cap >= kMaxWavesPerCu / waves ? 0 : (cap < 0 ? 0 : cap);
-    p.lds_bytes = p.resident_cap ? reserve_for_cap(p.ring_bytes, p.resident_cap, lds_budget)
-                                 : p.ring_bytes;
     p.path = TP_PATH_X4;
     if (n > 0 && align == TP_ALIGN_WORDS) {
         p.path = path_bits(in, out);
@@ -181,6 +175,12 @@ int plan_map(uintptr_t in, uintptr_t out, int64_t n, int op, int tile_elems, int
             (int64_t)((kRealignBytes - anchor % kRealignBytes) % kRealignBytes / 4);
         p.head = (int32_t)(to_boundary < n ? to_boundary : n);
     }
+    const int waves = p.threads / 64;
+    const int cap = resident_cap == 0 ? map_policy_resident_cap(op, tile_elems, stages, tpb, waves)
+                                      : resident_cap;
+    p.resident_cap = cap >= kMaxWavesPerCu / waves ? 0 : (cap < 0 ? 0 : cap);
+    p.lds_bytes = p.resident_cap ? reserve_for_cap(p.ring_bytes, p.resident_cap, lds_budget)
+                                 : p.ring_bytes;
     const bool load_x4 = !(p.path & TP_PATH_SCALAR_LOAD);
     const bool store_x4 = !(p.path & TP_PATH_SCALAR_STORE);
     if (schedule == TP_SCHED_ROLE_SPLIT) {
@@ -230,7 +230,7 @@ int plan_map_2d(uintptr_t src, int64_t src_stride, uintptr_t dst, int64_t dst_st
     if (box_rows < 1 || box_cols < 4 || (box_rows & (box_rows - 1)) || (box_cols & (box_cols - 1)) ||
         !valid_tile((int)(tile > 8192 ? 0 : tile)))
         return TP_ERR_INVALID_ARG;
-    const int tpb = resolve_tiles_per_block(tiles_per_block, kDefaultMapTilesPerBlock);
+    const int tpb = resolve_tiles_per_block(tiles_per_block, kDefaultMap2dBoxesPerBlock);
     if (tpb < 0)
         return TP_ERR_INVALID_ARG;
     const MapGeometry g = map_geometry((int)tile);

@@ -217,7 +217,7 @@ def pipelined_map(x, y=None, op: str = "scale2", tile_elems: int = 1024, stages:
     """y[i] = op(x[i]) for float32 GPU tensors (any shape, contiguous).
 
     Each workgroup streams tiles_per_block consecutive tiles (0: the
-    library default of 2). resident_cap bounds the workgroups per CU
+    library default, 4 for tiles of at most 512 floats, else 2). resident_cap bounds the workgroups per CU
     (0: the library's policy, -1: no bound, k: about k). schedule "uniform"
     (every wave loads its own part) or "role_split" (one wave loads, the
     others compute). align "realign" (16-byte accesses at any 4-byte

@@ -65,7 +65,7 @@ def test_stored_traffic_is_tied_to_the_sources():
     bench = _bench()
     h = bench.kernel_source_hash()
     assert len(h) == 16 and int(h, 16) >= 0
-    entry = bench.stored_traffic("map_scale2_n268435456_t256_s2_T2")
+    entry = bench.stored_traffic("map_scale2_n268435456_t256_s2_T4")
     # either the stored counters describe the current sources, or nothing is reported
     assert entry is None or 2 * (1 << 30) <= entry < 2 * (1 << 30) * 1.01
 

@@ -124,7 +124,7 @@ def test_role_split_schedule():
 
 
 def test_full_size_map_launches():
-    # the step (2^28 floats, tile 256, 2 stages, runs of 2: 524288 workgroups)
+    # the step (2^28 floats, tile 256, 2 stages, runs of 4: 262144 workgroups)
     # and the 4-byte-offset sweep point, on full-size buffers whose untouched
     # pages are never allocated: the first workgroups, one in the middle and
     # the last ones run
@@ -146,7 +146,8 @@ def test_full_size_map_launches():
             x[lo:hi] = np.random.default_rng(b).random(hi - lo, dtype=np.float32) * 2 - 1
         plan = emu.pipelined_map(x, y, "scale2", 256, 2, 0, blocks=blocks,
                                  regions=[(x, False), (y, True)], policy=in_off)
-        assert plan.grid == (524288 if in_off == 0 else plan.grid) and plan.tiles_per_block == 2
+        assert plan.tiles_per_block == 4
+        assert plan.grid == (262144 if in_off == 0 else plan.grid)
         for b in blocks:
             lo = plan.head + b * per
             hi = min(n, plan.head + (b + 1) * per)

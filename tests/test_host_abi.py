@@ -62,10 +62,17 @@ def test_map_plan_geometry_runs():
 
 
 def test_map_plan_default_run_length():
+    # runs of 4 tiles of at most 512 floats (4-8 KiB), of 2 larger tiles
     p = tp.plan_map(A, B, 1 << 28, "scale2", 256, 2, 0)
-    assert p.tiles_per_block == 2 and p.grid == (1 << 20) // 2
+    assert p.tiles_per_block == 4 and p.grid == (1 << 20) // 4
+    for tile, run in ((512, 4), (1024, 2), (2048, 2), (8192, 2)):
+        assert tp.plan_map(A, B, 1 << 28, "horner32", tile, 2, 0).tiles_per_block == run, tile
+    # the same whatever the alignment of the input
+    assert tp.plan_map(A + 4, B, 1 << 28, "scale2", 256, 2, 0).tiles_per_block == 4
     p = tp.plan_map(A, B, 5000, "scale2", 1024, 2, 0)
     assert (p.num_tiles, p.grid) == (5, 3)
+    # the 2-D map keeps runs of 2 boxes
+    assert tp.plan_map_2d(A, 1024, B, 1024, 64, 1024, "scale2", 1, 256).tiles_per_block == 2
     # the chunk copy's default run is max(S-1, m) tiles, m = 1, 2, 8 for 16-,
     # 8- and 4-byte chunks: with 16-byte chunks the prologue holds the whole run
     for width, stages, run in ((16, 1, 1), (16, 2, 1), (16, 3, 2), (16, 4, 3), (16, 8, 7),
@@ -199,15 +206,16 @@ def _reserve(cap, ring, budget=160 * KIB):
 
 
 def test_map_residency_policy_values():
-    # worked by hand from the rule: cap = round(28 KiB (1 + 1/T) / ((a + 1) tile bytes)),
+    # worked by hand from the rule: cap = round(27 KiB (1 + 1/T) / ((a + 1) tile bytes)),
     # a = mean over the run of min(S, tiles left), at least 4 workgroups and 8 waves
     cases = [  # tile, S, T, cap
-        (256, 2, 2, 17),     # a = 1.5: 43008 / (2.5 * 1024) = 16.8
-        (256, 1, 2, 21),     # a = 1: 43008 / 2048 = 21
-        (256, 4, 8, 8),      # a = 26/8: 32256 / (4.25 * 1024) = 7.4 -> 7, raised to 8 waves
-        (1024, 2, 2, 4),     # 43008 / (2.5 * 4096) = 4.2
-        (1024, 4, 8, 4),     # 32256 / (4.25 * 4096) = 1.9, raised to 4 workgroups
-        (512, 4, 4, 5),      # a = 2.5: 35840 / (3.5 * 2048) = 5.0
+        (256, 2, 4, 12),     # the step: a = 1.75: 34560 / (2.75 * 1024) = 12.3
+        (256, 2, 2, 16),     # a = 1.5: 41472 / (2.5 * 1024) = 16.2
+        (256, 1, 2, 20),     # a = 1: 41472 / 2048 = 20.3
+        (256, 4, 8, 8),      # a = 26/8: 31104 / (4.25 * 1024) = 7.1 -> 7, raised to 8 waves
+        (1024, 2, 2, 4),     # 41472 / (2.5 * 4096) = 4.05
+        (1024, 4, 8, 4),     # 31104 / (4.25 * 4096) = 1.8, raised to 4 workgroups
+        (512, 4, 4, 5),      # a = 2.5: 34560 / (3.5 * 2048) = 4.8
         (2048, 2, 2, 0),     # two 16-byte loads per lane per tile: not bounded
         (4096, 4, 2, 0),
     ]
