@@ -61,6 +61,8 @@ def _load():
     lib.oracle_chunk_copy_w.restype = None
     lib.oracle_map_2d.argtypes = [p, i64, p, i64, i64, ctypes.c_int, i64, i64]
     lib.oracle_map_2d.restype = None
+    lib.oracle_workgroup_copy.argtypes = [p, p, i64, i64]
+    lib.oracle_workgroup_copy.restype = None
     _lib = lib
     return lib
 
@@ -206,3 +208,23 @@ def chunk_copy(src: np.ndarray, dst: np.ndarray, pred: np.ndarray | None = None,
                 (_ptr(src), _ptr(res), chunk_bytes, *(_ptr(m) for m in meta)), n,
                 threads or default_threads())
     return res.reshape(dst.shape)
+
+
+# ------------------------------------------------------- copies between workgroups
+WORKGROUP_CHUNK = 256
+
+
+def workgroup_copy(src: np.ndarray, dst: np.ndarray, threads: int | None = None) -> np.ndarray:
+    """Return a new array: dst after every group k >= 1 received chunk k - 1 of
+    src (256-byte chunks; dst chunk 0 unchanged). src and dst are uint8 arrays
+    of the same whole number of chunks."""
+    src = _contig(src.reshape(-1), np.uint8)
+    out = _contig(dst.reshape(-1), np.uint8).copy()
+    if src.size != out.size or src.size % WORKGROUP_CHUNK:
+        raise ValueError("src and dst must hold the same whole number of 256-byte chunks")
+    n = src.size // WORKGROUP_CHUNK
+    rs = _ranges(n, threads or default_threads(), min_block=1 << 12)
+    fn = _load().oracle_workgroup_copy
+    with ThreadPoolExecutor(max_workers=max(1, len(rs))) as ex:
+        list(ex.map(lambda r: fn(_ptr(src), _ptr(out), r[0], r[1]), rs))
+    return out

@@ -1,8 +1,8 @@
 /*
  * CPU oracle for libtilepipe: TEST INFRASTRUCTURE ONLY.
  *
- * Plain, slow, obviously correct C definitions of what the three GPU entry
- * points compute. Only the test-suite, the smoke check and the CPU-baseline
+ * Plain, slow, obviously correct C definitions of what the GPU entry points
+ * compute. Only the test-suite, the smoke check and the CPU-baseline
  * leg of the benchmark load this file's library; the product path never does.
  * It shares no code, header, table or helper with the HIP library: it has its
  * own coefficient table, its own loops and no notion of tiles, stages, lanes
@@ -189,4 +189,24 @@ void oracle_chunk_copy(const uint8_t *src, uint8_t *dst,
                        const uint8_t *ignore_src, int64_t lo, int64_t hi)
 {
     oracle_chunk_copy_w(src, dst, 16, pred, src_size, ignore_src, lo, hi);
+}
+
+/*
+ * Copies between workgroups ("Asynchronous Copies", section "Copies between
+ * CTAs": one group's shared-memory chunk of 256 bytes is copied into another
+ * group's shared memory, and the receiver waits until those bytes have
+ * arrived before it reads them). Over n chunks, group k holds chunk k of src
+ * and hands it to group k + 1, which writes what it received as chunk k + 1
+ * of dst:
+ *   dst[k] = src[k - 1]  (256 bytes each),  1 <= k < n;
+ * dst chunk 0 receives nothing and is not written. src and dst must not
+ * overlap. [lo, hi) ranges over the receiving chunks k.
+ */
+void oracle_workgroup_copy(const uint8_t *src, uint8_t *dst, int64_t lo, int64_t hi)
+{
+    for (int64_t k = lo; k < hi; ++k) {
+        if (k < 1)
+            continue;
+        memcpy(dst + 256 * k, src + 256 * (k - 1), 256);
+    }
 }

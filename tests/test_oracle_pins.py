@@ -423,3 +423,53 @@ def test_workload_generators_are_deterministic_and_in_range():
     assert abs(inp.pred.numpy().mean() - 0.9) < 0.01
     assert abs(inp.ignore_src.numpy().mean() - 0.01) < 0.003
     assert np.all(inp.dst_init.numpy().view(np.uint32) == 0xDEADBEEF)
+
+
+# ------------------------------------------------------- copies between workgroups
+def _chunk_index_pattern(n):
+    """n 256-byte chunks, chunk k made of the 32-bit word k repeated."""
+    return np.repeat(np.arange(n, dtype=np.uint32), 64).view(np.uint8)
+
+
+def test_workgroup_copy_closed_form():
+    # "Copies between CTAs": each group's 256-byte chunk arrives in the next
+    # group, which writes it: output chunk k holds the word k - 1 for k >= 1,
+    # and chunk 0, which no group sends to, keeps its prior contents
+    for n in (2, 3, 64, 1000):
+        src = _chunk_index_pattern(n)
+        fill = np.full(n * 64, 0xDEADBEEF, np.uint32).view(np.uint8)
+        out = oracle.workgroup_copy(src, fill).view(np.uint32).reshape(n, 64)
+        assert np.all(out[0] == 0xDEADBEEF)
+        assert np.array_equal(out[1:], np.repeat(np.arange(n - 1, dtype=np.uint32)[:, None], 64, 1))
+
+
+def test_workgroup_copy_against_numpy_roll():
+    # a library routine: every chunk but the first equals numpy's roll of the
+    # source by one chunk; random bytes catch a partial chunk or a byte order slip
+    rng = np.random.default_rng(3)
+    for n in (2, 7, 513):
+        src = rng.integers(0, 256, n * 256, dtype=np.uint8)
+        dst = rng.integers(0, 256, n * 256, dtype=np.uint8)
+        out = oracle.workgroup_copy(src, dst, threads=3)
+        rolled = np.roll(src.reshape(n, 256), 1, axis=0)
+        assert np.array_equal(out.reshape(n, 256)[1:], rolled[1:])
+        assert np.array_equal(out[:256], dst[:256])
+
+
+def test_workgroup_copy_iterated_fills_from_chunk_zero():
+    # invariant: feeding the output back n - 1 times (dst = the previous
+    # output) carries chunk 0 into every chunk
+    n = 9
+    x = _chunk_index_pattern(n).copy()
+    for _ in range(n - 1):
+        x = oracle.workgroup_copy(x, x)
+    assert np.all(x.view(np.uint32) == 0)
+
+
+def test_workgroup_copy_degenerate_sizes():
+    # no chunk or a single chunk: no group receives anything
+    assert oracle.workgroup_copy(np.zeros(0, np.uint8), np.zeros(0, np.uint8)).size == 0
+    one = np.arange(256, dtype=np.uint8)
+    assert np.array_equal(oracle.workgroup_copy(np.zeros(256, np.uint8), one), one)
+    with pytest.raises(ValueError):
+        oracle.workgroup_copy(np.zeros(300, np.uint8), np.zeros(300, np.uint8))
