@@ -580,6 +580,38 @@ def chunk_copy_row(tp, workloads, torch, np, dev, cpu_seconds):
     return out
 
 
+def workgroup_copy_row(tp, torch, np, dev):
+    """Copies between workgroups over 2^20 chunks of 256 bytes (256 MiB): each
+    of 2^20 one-wave workgroups hands its chunk to the next through a staging
+    slot and a device-scope flag. GB/s on the algorithmic bytes (each handed
+    chunk read once and written once, 512 B per chunk); the staging slot adds
+    another 512 B per chunk (written, then read) that the definition does not
+    need. Parity of the whole destination against the definition."""
+    n = 1 << 20
+    g = torch.Generator().manual_seed(10)
+    src = torch.randint(0, 256, (n * 256,), generator=g, dtype=torch.uint8).to(dev)
+    dst = torch.zeros_like(src)
+    ws = torch.empty(tp.workgroup_copy_workspace_bytes(n), dtype=torch.uint8, device=dev)
+    status = torch.empty(1, dtype=torch.int32, device=dev)
+    f = lambda: tp.workgroup_copy(src, dst, ws, status)
+    f()
+    torch.cuda.synchronize()
+    ok = int(status.item()) == 0 and bool(torch.equal(dst[256:], src[:-256]))
+    gpu_warmup(f)
+    per, _ = time_launches(f, 2, 20)
+    us = median(per) * 1e3
+    alg = 512 * (n - 1)
+    out = {"n_chunks": n, "chunk_bytes": 256, "us_per_call": round(us, 1),
+           "GBs_algorithmic": round(alg / (us * 1e-6) / 1e9, 1),
+           "GBs_with_staging": round(2 * alg / (us * 1e-6) / 1e9, 1),
+           "status_ok_and_parity": ok,
+           "note": "one call = the clearing kernel plus the hand-off kernel; 1 KiB moves per "
+                   "chunk (source, staging write, staging read, destination), 512 B of it "
+                   "algorithmic"}
+    log(f"workgroup_copy: {out}")
+    return out
+
+
 def chunk_cpu_baseline(inp, seconds):
     """The oracle's chunk copy (untuned) on the host cores over the same 2^26
     chunks: whole passes for about `seconds`, GB/s on the algorithmic bytes."""
@@ -1062,6 +1094,8 @@ def extra_rows(args, tp, workloads, torch, np, dev, x_host, xbuf, y):
 
     # predicated chunk copy: 2^26 chunks
     rows["chunk_copy"] = chunk_copy_row(tp, workloads, torch, np, dev, args.cpu_seconds)
+
+    rows["workgroup_copy"] = workgroup_copy_row(tp, torch, np, dev)
 
     # row exchange 64x4 (launch-bound)
     a = workloads.arange_rows(64).to(dev)

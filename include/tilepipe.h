@@ -301,6 +301,49 @@ TP_API int tp_chunk_copy_ex(const void *src, void *dst, int64_t n_chunks, int ch
                             void *stream, int *path_out);
 
 /*
+ * Copies between workgroups ("Asynchronous Copies", section "Copies between
+ * CTAs": one group copies a 256-byte chunk of its shared memory into another
+ * group's, and the receiver waits until the bytes have arrived before reading
+ * them). Over n_chunks chunks of 256 bytes, workgroup k copies chunk k of src
+ * into its LDS and hands it to workgroup k + 1, which writes what it received
+ * as chunk k + 1 of dst:
+ *     dst[k] = src[k - 1]   (256 bytes each),  1 <= k < n_chunks;
+ * chunk 0 of dst receives nothing and is not written. CDNA4 workgroups cannot
+ * address each other's LDS, so the chunk passes through a staging slot in
+ * `workspace`. The sender writes the slot at device scope (coherent across
+ * the XCDs' L2s), waits for those stores, then sets a flag; the receiver polls
+ * the flag and copies the slot into its LDS with device-scope loads before
+ * storing it. A workgroup waits only for the one numbered just below it,
+ * which was dispatched before it.
+ *   src, dst: device buffers of n_chunks x 256 bytes, 4-byte aligned; dst ==
+ *     src is allowed (each workgroup reads its own chunk before its receiver
+ *     role writes it); a partial overlap is TP_ERR_OVERLAP.
+ *   workspace: caller-owned device memory of at least
+ *     tp_workgroup_copy_workspace_bytes(n_chunks) bytes, 4-byte aligned:
+ *     n_chunks flag words, then 256-byte staging slots. The call clears the
+ *     flags itself (a kernel on `stream` before the hand-off), so the
+ *     workspace needs no preparation. Calls that share a workspace must not
+ *     overlap in time.
+ *   status: caller-owned device int32. The call sets it to 0 and a receiver
+ *     that gives up waiting sets it to 1; read it after the stream has
+ *     finished. 1 means some dst chunks were not written.
+ *   spin_limit: polls of its sender's flag before a receiver gives up
+ *     (0 = the default of 65536; at most 2^24). A receiver that finds the
+ *     status set stops polling too, so the kernel always finishes.
+ * n_chunks 0: TP_OK, nothing launched. More than 2^26 chunks, a missing
+ * pointer or a short workspace: TP_ERR_INVALID_ARG; pointers not 4-byte
+ * aligned: TP_ERR_MISALIGNED; workspace or status overlapping src or dst, or
+ * each other: TP_ERR_OVERLAP.
+ */
+TP_API int tp_workgroup_copy(const void *src, void *dst, int64_t n_chunks, void *workspace,
+                             int64_t workspace_bytes, int32_t *status, int spin_limit,
+                             void *stream);
+
+/* Bytes of workspace tp_workgroup_copy needs for n_chunks chunks (-1 if
+ * n_chunks is out of range). */
+TP_API int64_t tp_workgroup_copy_workspace_bytes(int64_t n_chunks);
+
+/*
  * Host-only planning: the same validation and launch plan as the entry point
  * of the same name, for the given pointer values and LDS budget (bytes per
  * workgroup), without touching any device. Pointers are only inspected for
@@ -321,6 +364,9 @@ TP_API int tp_plan_chunk_copy(const void *src, const void *dst, int64_t n_chunks
                               int chunk_bytes, const void *pred, const void *src_size,
                               const void *ignore_src, int stages, int tiles_per_block,
                               int64_t lds_budget, tp_plan *plan);
+TP_API int tp_plan_workgroup_copy(const void *src, const void *dst, int64_t n_chunks,
+                                  const void *workspace, int64_t workspace_bytes,
+                                  const int32_t *status, int spin_limit, tp_plan *plan);
 
 #ifdef __cplusplus
 }

@@ -47,7 +47,7 @@ INSTANCES = [
       f"-DTP_INST_FN=launch_{fam}_{op}_s{lo}_{hi}"])
     for fam in ("map2d", "map_split", "map") for lo, hi in reversed(_HALVES) for op, macro in _OPS
 ]
-HIP_SOURCES = ["tp_chunk_copy.hip", "tp_row_shift.hip", "tp_api.cpp"]
+HIP_SOURCES = ["tp_chunk_copy.hip", "tp_row_shift.hip", "tp_wg_copy.hip", "tp_api.cpp"]
 CXX_SOURCES = ["tp_plan.cpp"]
 
 

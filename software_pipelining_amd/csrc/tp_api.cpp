@@ -298,4 +298,46 @@ TP_API int tp_chunk_copy_ex(const void *src, void *dst, int64_t n_chunks, int ch
     return finish_launch(tp::launch_chunk_copy(plan, p, stream));
 }
 
+TP_API int64_t tp_workgroup_copy_workspace_bytes(int64_t n_chunks)
+{
+    return n_chunks < 0 || n_chunks > tp::kWgMaxChunks ? -1 : tp::wg_workspace_bytes(n_chunks);
+}
+
+TP_API int tp_plan_workgroup_copy(const void *src, const void *dst, int64_t n_chunks,
+                                  const void *workspace, int64_t workspace_bytes,
+                                  const int32_t *status, int spin_limit, tp_plan *plan)
+{
+    return tp::plan_workgroup_copy((uintptr_t)src, (uintptr_t)dst, n_chunks,
+                                   (uintptr_t)workspace, workspace_bytes, (uintptr_t)status,
+                                   spin_limit, plan);
+}
+
+TP_API int tp_workgroup_copy(const void *src, void *dst, int64_t n_chunks, void *workspace,
+                             int64_t workspace_bytes, int32_t *status, int spin_limit,
+                             void *stream)
+{
+    tp_plan plan;
+    int st = tp::plan_workgroup_copy((uintptr_t)src, (uintptr_t)dst, n_chunks,
+                                     (uintptr_t)workspace, workspace_bytes, (uintptr_t)status,
+                                     spin_limit, &plan);
+    if (st != TP_OK)
+        return st;
+    if (n_chunks == 0)
+        return TP_OK;
+    int64_t lds = 0;
+    if ((st = current_device(&lds)) != TP_OK)
+        return st;
+    if (plan.lds_bytes > lds)
+        return TP_ERR_LDS_BUDGET;
+    tp::WgCopyParams p{};
+    p.src = static_cast<const uint8_t *>(src);
+    p.dst = static_cast<uint8_t *>(dst);
+    p.flags = static_cast<uint32_t *>(workspace);
+    p.stage = static_cast<uint8_t *>(workspace) + tp::wg_stage_offset(n_chunks);
+    p.status = status;
+    p.n_chunks = n_chunks;
+    p.spin_limit = spin_limit == 0 ? tp::kWgDefaultSpinLimit : (uint32_t)spin_limit;
+    return finish_launch(tp::launch_workgroup_copy(plan, p, stream));
+}
+
 }  // extern "C"

@@ -162,6 +162,56 @@ __device__ __forceinline__ void store_b32(const BufferRes &r, uint32_t voff, uin
                  : "memory");
 }
 
+// ------------------------------------------- hand-offs between workgroups
+// A workgroup that hands data to another, possibly on another XCD, reads and
+// writes it at device scope (sc1); the L2s of the XCDs are not coherent with
+// one another. Device-scope loads and stores are what the compiler itself
+// emits for relaxed atomic loads and stores at device ("agent") scope on
+// gfx950, with no L2 write-back or invalidate: they are coherent across XCDs
+// on their own. Their order comes from the waits: a sender's data stores have
+// all completed (vmcnt 0) before it stores the flag, and a receiver issues its
+// data loads only after the flag load has returned. The compiler's release
+// and acquire sequences add an L2 write-back (buffer_wbl2) and invalidate
+// (buffer_inv) for ordinary stores and loads around the flag; those act on the
+// whole L2 of an XCD, and with one hand-off per workgroup they took 19 ms for
+// 2^20 chunks, against the device-scope data accesses used here.
+
+// A 4-byte LDS-DMA load at device scope (sc1): lane l's word lands at
+// m0 + 4 * l.
+__device__ __forceinline__ void dma_b32_device(const BufferRes &r, uint32_t voff, uint32_t m0)
+{
+    asm volatile("s_mov_b32 m0, %2\n\t"
+                 "s_nop 4\n\t"
+                 "buffer_load_dword %0, %1, 0 offen sc1 lds"
+                 :
+                 : "v"(voff), "s"(sgpr_res(r)), "s"(m0)
+                 : "memory");
+}
+
+// A 4-byte load at device scope into a register, complete when this returns
+// (the wait is part of the block, so the compiler sees the value only then).
+__device__ __forceinline__ uint32_t load_b32_device(const BufferRes &r, uint32_t voff)
+{
+    uint32_t v;
+    asm volatile("s_nop 4\n\t"
+                 "buffer_load_dword %0, %1, %2, 0 offen sc1\n\t"
+                 "s_waitcnt vmcnt(0)"
+                 : "=v"(v)
+                 : "v"(voff), "s"(sgpr_res(r))
+                 : "memory");
+    return v;
+}
+
+// A 4-byte store at device scope (a flag or status word).
+__device__ __forceinline__ void store_b32_device(const BufferRes &r, uint32_t voff, uint32_t v)
+{
+    asm volatile("s_nop 4\n\t"
+                 "buffer_store_dword %0, %1, %2, 0 offen sc1"
+                 :
+                 : "v"(v), "v"(voff), "s"(sgpr_res(r))
+                 : "memory");
+}
+
 // ------------------------------------------------------------ completion
 // Wait until at most K of this wave's vector-memory operations are pending.
 template <int K>
@@ -238,6 +288,20 @@ struct GpuEngine {
         vm_wait<K>();
     }
     __device__ __forceinline__ void barrier() const { block_sync(); }
+    __device__ __forceinline__ void dma_b32_device(const BufferRes &r, uint32_t voff, uint32_t m0) const
+    {
+        dev::dma_b32_device(r, voff, m0);
+    }
+    __device__ __forceinline__ uint32_t load_b32_device(const BufferRes &r, uint32_t voff) const
+    {
+        return dev::load_b32_device(r, voff);
+    }
+    __device__ __forceinline__ void store_b32_device(const BufferRes &r, uint32_t voff, uint32_t v) const
+    {
+        dev::store_b32_device(r, voff, v);
+    }
+    // a short pause between polls of a flag
+    __device__ __forceinline__ void pause() const { __builtin_amdgcn_s_sleep(1); }
 };
 
 // The engine of a kernel whose dynamic LDS is `lds`. blockDim.x is read here,

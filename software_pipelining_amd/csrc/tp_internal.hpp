@@ -187,6 +187,29 @@ inline ChunkParams chunk_params(const tp_plan &plan, const void *src, void *dst,
     return p;
 }
 
+// ------------------------------------------------ copies between workgroups
+constexpr int kWgChunkBytes = 256;             // the chunk one workgroup hands on
+constexpr int64_t kWgMaxChunks = int64_t(1) << 26;
+constexpr uint32_t kWgDefaultSpinLimit = 1u << 16;   // polls of a flag before giving up
+constexpr uint32_t kWgMaxSpinLimit = 1u << 24;
+constexpr int64_t kWgClearThreads = 256;       // lanes of a workgroup of the clearing kernel
+
+// Workspace of a copy between n workgroups: n flag words, then, from the next
+// 256-byte boundary, n staging slots of 256 bytes.
+TP_HD constexpr int64_t wg_stage_offset(int64_t n) { return (4 * n + 255) / 256 * 256; }
+TP_HD constexpr int64_t wg_workspace_bytes(int64_t n) { return n <= 0 ? 0 : wg_stage_offset(n) + kWgChunkBytes * n; }
+
+struct WgCopyParams {
+    const uint8_t *src;
+    uint8_t *dst;
+    uint8_t *stage;          // n staging slots of kWgChunkBytes
+    uint32_t *flags;         // n words: flags[k] != 0 once chunk k is staged
+    int32_t *status;         // 0, or 1 once a receiver gave up waiting
+    int64_t n_chunks;
+    uint32_t spin_limit;     // polls of a flag before a receiver gives up
+    uint32_t pad;
+};
+
 // -------------------------------------------------------------- row shift
 struct RowShiftParams {
     const float *a;
@@ -213,6 +236,13 @@ int plan_map_2d(uintptr_t src, int64_t src_stride, uintptr_t dst, int64_t dst_st
 int plan_chunk_copy(uintptr_t src, uintptr_t dst, int64_t n_chunks, int chunk_bytes,
                     uintptr_t pred, uintptr_t src_size, uintptr_t ignore_src, int stages,
                     int tiles_per_block, int64_t lds_budget, tp_plan *plan);
+
+// Validates a copy between workgroups (the workspace is caller memory of
+// workspace_bytes; spin_limit 0 means the default) and plans its main kernel:
+// n_chunks one-wave workgroups with 512 bytes of LDS.
+int plan_workgroup_copy(uintptr_t src, uintptr_t dst, int64_t n_chunks, uintptr_t workspace,
+                        int64_t workspace_bytes, uintptr_t status, int64_t spin_limit,
+                        tp_plan *plan);
 
 // TP_OK for a device whose architecture name is gfx950 (optionally followed by
 // ":feature..." suffixes), TP_ERR_UNSUPPORTED_DEVICE for any other name.
@@ -250,5 +280,8 @@ int launch_map2d_horner32_s5_8(const tp_plan &plan, const Map2dParams &p, void *
 int launch_map2d_copy_s1_4(const tp_plan &plan, const Map2dParams &p, void *stream);
 int launch_map2d_copy_s5_8(const tp_plan &plan, const Map2dParams &p, void *stream);
 int launch_chunk_copy(const tp_plan &plan, const ChunkParams &p, void *stream);
+// The clearing kernel (flags and status to zero), then, for two chunks or
+// more, the hand-off kernel.
+int launch_workgroup_copy(const tp_plan &plan, const WgCopyParams &p, void *stream);
 
 }  // namespace tp

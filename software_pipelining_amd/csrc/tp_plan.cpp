@@ -371,6 +371,47 @@ int plan_chunk_copy(uintptr_t src, uintptr_t dst, int64_t n_chunks, int chunk_by
     return TP_OK;
 }
 
+int plan_workgroup_copy(uintptr_t src, uintptr_t dst, int64_t n_chunks, uintptr_t workspace,
+                        int64_t workspace_bytes, uintptr_t status, int64_t spin_limit,
+                        tp_plan *plan)
+{
+    if (n_chunks < 0 || n_chunks > kWgMaxChunks)
+        return TP_ERR_INVALID_ARG;
+    if (spin_limit < 0 || spin_limit > (int64_t)kWgMaxSpinLimit)
+        return TP_ERR_INVALID_ARG;
+    tp_plan p;
+    memset(&p, 0, sizeof p);
+    p.stages = 1;
+    p.tile_units = kWgChunkBytes;
+    p.threads = 64;
+    p.lane_chunks = 1;
+    p.tiles_per_block = 1;
+    p.lds_bytes = 2 * kWgChunkBytes;
+    p.ring_bytes = p.lds_bytes;
+    p.path = TP_PATH_SCALAR;
+    if (n_chunks > 0) {
+        const int64_t need = wg_workspace_bytes(n_chunks);
+        if (!src || !dst || !workspace || !status || workspace_bytes < need)
+            return TP_ERR_INVALID_ARG;
+        if (src % 4 || dst % 4 || workspace % 4 || status % 4)
+            return TP_ERR_MISALIGNED;
+        const uint64_t bytes = (uint64_t)n_chunks * kWgChunkBytes;
+        if (src != dst && overlaps(src, bytes, dst, bytes))
+            return TP_ERR_OVERLAP;
+        const uintptr_t data[2] = {src, dst};
+        for (uintptr_t a : data)
+            if (overlaps(a, bytes, workspace, (uint64_t)need) || overlaps(a, bytes, status, 4))
+                return TP_ERR_OVERLAP;
+        if (overlaps(workspace, (uint64_t)need, status, 4))
+            return TP_ERR_OVERLAP;
+        p.num_tiles = n_chunks;
+        p.grid = n_chunks;
+    }
+    if (plan)
+        *plan = p;
+    return TP_OK;
+}
+
 void horner32_coefficients(float c[32])
 {
     for (int k = 0; k < 32; ++k)

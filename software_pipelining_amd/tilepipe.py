@@ -137,6 +137,9 @@ def _load():
         "tp_map_2d": ([vp, i64, vp, i64, i64, i64, i32, i32, i32, i32, i32, i32, vp, ip], i32),
         "tp_plan_map_2d": ([vp, i64, vp, i64, i64, i64, i32, i32, i32, i32, i32, i32, i64, pp],
                            i32),
+        "tp_workgroup_copy": ([vp, vp, i64, vp, i64, vp, i32, vp], i32),
+        "tp_workgroup_copy_workspace_bytes": ([i64], i64),
+        "tp_plan_workgroup_copy": ([vp, vp, i64, vp, i64, vp, i32, pp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -313,6 +316,47 @@ def chunk_copy(src, dst, pred=None, src_size=None, ignore_src=None, stages: int 
     return Path(path.value)
 
 
+def workgroup_copy_workspace_bytes(n_chunks: int) -> int:
+    """Bytes of workspace a copy between n_chunks workgroups needs."""
+    v = _load().tp_workgroup_copy_workspace_bytes(n_chunks)
+    if v < 0:
+        raise ValueError("n_chunks out of range")
+    return v
+
+
+def workgroup_copy(src, dst, workspace=None, status=None, spin_limit: int = 0, stream=None):
+    """Copies between workgroups: chunk k of dst (256 bytes) receives chunk
+    k - 1 of src, handed from workgroup k - 1 to workgroup k; dst chunk 0 is
+    not written. src, dst: uint8 GPU tensors of the same whole number of
+    256-byte chunks. workspace: uint8 GPU tensor of at least
+    workgroup_copy_workspace_bytes(n) bytes (allocated here when None).
+    status: int32 GPU tensor of one element (allocated when None), 0 after the
+    stream has run the call, 1 if some receiver gave up waiting. Returns the
+    status tensor (reading it synchronizes)."""
+    import torch
+    _require(src, torch.uint8, "src")
+    _require(dst, torch.uint8, "dst")
+    if src.numel() != dst.numel() or src.numel() % 256:
+        raise ValueError("src and dst must hold the same whole number of 256-byte chunks")
+    n = src.numel() // 256
+    if workspace is None:
+        workspace = torch.empty(max(1, workgroup_copy_workspace_bytes(n)), dtype=torch.uint8,
+                                device=src.device)
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=src.device)
+    _require(workspace, torch.uint8, "workspace")
+    _require(status, torch.int32, "status")
+    _same_device(src, dst, workspace, status)
+    with torch.cuda.device(src.device):
+        st = _load().tp_workgroup_copy(ctypes.c_void_p(src.data_ptr()),
+                                       ctypes.c_void_p(dst.data_ptr()), n,
+                                       ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                       ctypes.c_void_p(status.data_ptr()), spin_limit,
+                                       _stream_handle(src, stream))
+    _check(st, "tp_workgroup_copy")
+    return status
+
+
 # --------------------------------------------------------- host-only plans
 _NO_BUDGET = (1 << 62)
 
@@ -369,3 +413,13 @@ def plan_chunk_copy(src_ptr: int, dst_ptr: int, n_chunks: int, pred_ptr: int = 0
                                     ctypes.c_void_p(ignore_ptr or None), stages, tiles_per_block,
                                     lds_budget, ctypes.byref(cp))
     return _plan(st, cp, "tp_plan_chunk_copy")
+
+
+def plan_workgroup_copy(src_ptr: int, dst_ptr: int, n_chunks: int, workspace_ptr: int,
+                        workspace_bytes: int, status_ptr: int, spin_limit: int = 0) -> Plan:
+    cp = _CPlan()
+    st = _load().tp_plan_workgroup_copy(ctypes.c_void_p(src_ptr), ctypes.c_void_p(dst_ptr),
+                                        n_chunks, ctypes.c_void_p(workspace_ptr or None),
+                                        workspace_bytes, ctypes.c_void_p(status_ptr or None),
+                                        spin_limit, ctypes.byref(cp))
+    return _plan(st, cp, "tp_plan_workgroup_copy")

@@ -208,3 +208,18 @@ def row_shift(a, b, *, policy=0, seed=0, wait_bias=0, lds_base=0, regions=None):
         regions = [(a, False), (b, True)] if a.ctypes.data != b.ctypes.data else [(b, True)]
     args = (_ptr(a), _ptr(b), ctypes.c_int64(a.shape[0]))
     return _call("emu_row_shift", args, regions, policy, seed, wait_bias, lds_base, None)
+
+
+def workgroup_copy(src, dst, workspace, status, *, spin_limit=0, policy=0, seed=0, lds_base=0,
+                   blocks=None, regions=None):
+    """Copies between workgroups under the emulator on host numpy buffers
+    (uint8 src/dst/workspace, int32 status of one element). `blocks` orders
+    the hand-off kernel's workgroups (default: 0, 1, ...)."""
+    n = dst.nbytes // 256
+    if regions is None:
+        regions = [(src, False), (dst, True), (workspace, True), (status, True)]
+        if src.ctypes.data == dst.ctypes.data:
+            regions = regions[1:]
+    args = (_ptr(src), _ptr(dst), ctypes.c_int64(n), _ptr(workspace),
+            ctypes.c_int64(workspace.nbytes), _ptr(status), spin_limit)
+    return _call("emu_workgroup_copy", args, regions, policy, seed, 0, lds_base, blocks)

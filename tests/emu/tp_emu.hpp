@@ -97,19 +97,20 @@ struct Res {
     uint32_t num_records;
 };
 
-enum Kind { K_NONE, K_UNIFORM, K_LDS_LOAD, K_DMA, K_STORE, K_WAIT, K_BARRIER, K_DONE, K_LDS_STORE };
+enum Kind { K_NONE, K_UNIFORM, K_LDS_LOAD, K_DMA, K_STORE, K_WAIT, K_BARRIER, K_DONE, K_LDS_STORE,
+            K_LOAD };
 
 inline const char *kind_name(int k)
 {
     static const char *n[] = {"none", "readfirstlane", "LDS read", "LDS-DMA load", "store",
-                              "vmcnt wait", "barrier", "end", "LDS write"};
+                              "vmcnt wait", "barrier", "end", "LDS write", "register load"};
     return n[k];
 }
 
 struct Request {
     int kind = K_NONE;
     uint32_t a = 0, b = 0;   // UNIFORM: a = value; LDS_LOAD, LDS_STORE: a = offset, b = size;
-                             // DMA: a = voff, b = m0; STORE: a = voff; WAIT: a = K
+                             // DMA: a = voff, b = m0; STORE, LOAD: a = voff; WAIT: a = K
     int width = 0;           // DMA/STORE: 16, 4 or 1 bytes
     Res res{};
     uint8_t data[16];        // STORE and LDS_STORE data, LDS_LOAD result
@@ -306,6 +307,7 @@ class Emulator {
         }
         case K_LDS_LOAD: lds_read(w); break;
         case K_LDS_STORE: lds_write(w); break;
+        case K_LOAD: reg_load(w); break;
         case K_DMA: dma(w); break;
         case K_STORE: store(w); break;
         case K_WAIT: {
@@ -482,6 +484,30 @@ class Emulator {
             }
     }
 
+    // A 4-byte load into a register whose block ends with vmcnt(0): every
+    // earlier operation of the wave retires first, then each lane reads (0
+    // when its offset fails the range check).
+    void reg_load(Wave &w)
+    {
+        while (!w.vm.empty())
+            retire(w);
+        for (Lane *l : w.lanes) {
+            const Res &r = l->req.res;
+            const uint64_t o = l->req.a;
+            uint32_t v = 0;
+            if (o + 4 <= r.num_records) {
+                const uint64_t g = r.base + o;
+                if (!region_of(g, 4))
+                    fail("workgroup %u wave %d lane %u: load of 4 bytes at offset %llu of a "
+                         "buffer at %#llx (num_records %u) reads outside every buffer of the "
+                         "call", block, w.id, l->tid, (unsigned long long)o,
+                         (unsigned long long)r.base, r.num_records);
+                memcpy(&v, reinterpret_cast<const void *>(g), 4);
+            }
+            l->req.result = v;
+        }
+    }
+
     void store(Wave &w)
     {
         const int width = w.lanes[0]->req.width;
@@ -596,6 +622,20 @@ struct EmuEngine {
         q.kind = K_BARRIER;
         g_emu->post(q);
     }
+    // Device-scope accesses: the emulator's memory is one coherent store, so
+    // they are the plain ones.
+    void dma_b32_device(const Res &r, uint32_t voff, uint32_t m0) const { dma(r, voff, m0, 4); }
+    uint32_t load_b32_device(const Res &r, uint32_t voff) const
+    {
+        Request q;
+        q.kind = K_LOAD;
+        q.a = voff;
+        q.res = r;
+        g_emu->post(q);
+        return g_lane->req.result;
+    }
+    void store_b32_device(const Res &r, uint32_t voff, uint32_t v) const { store(r, voff, &v, 4); }
+    void pause() const {}
 };
 
 // Status of an entry point: a tp_status from planning, 0, or these.

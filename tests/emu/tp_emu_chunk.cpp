@@ -2,6 +2,7 @@
 #include "tp_chunk_copy.hpp"
 #include "tp_emu.hpp"
 #include "tp_row_shift.hpp"
+#include "tp_wg_copy.hpp"
 
 using emu::EmuEngine;
 
@@ -75,6 +76,46 @@ int emu_row_shift(const float *a, float *b, int64_t rows, const emu::Options *o,
     std::function<void()> body;
     emu::pick<0, 1, 2, 3>(plan.path, [&](auto q) { body = row_shift_body<q>(p); });
     return emu::launch(plan, *o, body, err, errlen);
+}
+
+// Copies between workgroups, planned as tp_workgroup_copy does: the clearing
+// kernel over every workgroup, then the hand-off kernel over the workgroups
+// of `o` in its order (the emulator runs one workgroup after another, so a
+// receiver run before its sender finds no flag and gives up after spin_limit
+// polls, as the GPU kernel would).
+int emu_workgroup_copy(const void *src, void *dst, int64_t n_chunks, void *workspace,
+                       int64_t workspace_bytes, int32_t *status, int spin_limit,
+                       const emu::Options *o, tp_plan *plan_out, char *err, int errlen)
+{
+    tp_plan plan;
+    const int st = tp::plan_workgroup_copy((uintptr_t)src, (uintptr_t)dst, n_chunks,
+                                           (uintptr_t)workspace, workspace_bytes,
+                                           (uintptr_t)status, spin_limit, &plan);
+    if (st != TP_OK)
+        return st;
+    *plan_out = plan;
+    if (n_chunks == 0)
+        return 0;
+    tp::WgCopyParams p{};
+    p.src = static_cast<const uint8_t *>(src);
+    p.dst = static_cast<uint8_t *>(dst);
+    p.flags = static_cast<uint32_t *>(workspace);
+    p.stage = static_cast<uint8_t *>(workspace) + tp::wg_stage_offset(n_chunks);
+    p.status = status;
+    p.n_chunks = n_chunks;
+    p.spin_limit = spin_limit == 0 ? tp::kWgDefaultSpinLimit : (uint32_t)spin_limit;
+    tp_plan clear = plan;
+    clear.threads = (int32_t)tp::kWgClearThreads;
+    clear.grid = (n_chunks + tp::kWgClearThreads - 1) / tp::kWgClearThreads;
+    clear.lds_bytes = 0;
+    emu::Options co = *o;
+    co.blocks = nullptr;
+    co.n_blocks = 0;
+    int r = emu::launch(clear, co, [p] { tp::dev::workgroup_copy_clear_body(EmuEngine{}, p); }, err,
+                        errlen);
+    if (r != 0 || n_chunks < 2)
+        return r;
+    return emu::launch(plan, *o, [p] { tp::dev::workgroup_copy_body(EmuEngine{}, p); }, err, errlen);
 }
 
 // The library's device check on an architecture name, as the device would

@@ -518,3 +518,39 @@ def test_header_is_plain_c():
         got = [int(v) for v in subprocess.run([exe], capture_output=True, text=True).stdout.split()]
         assert got[0] == ctypes.sizeof(tilepipe._CPlan)
         assert got[1:] == [getattr(tilepipe._CPlan, n).offset for n in fields]
+
+
+# ------------------------------------------------------- copies between workgroups
+def test_workgroup_copy_plan():
+    n = 1000
+    need = tp.workgroup_copy_workspace_bytes(n)
+    assert need == (4 * n + 255) // 256 * 256 + 256 * n
+    W, S = 0x7f8000000000, 0x7fc000000000
+    p = tp.plan_workgroup_copy(A, B, n, W, need, S)
+    assert (p.grid, p.threads, p.lds_bytes, p.tile_units) == (n, 64, 512, 256)
+    assert tp.plan_workgroup_copy(A, A, n, W, need, S).grid == n              # in place
+    assert tp.plan_workgroup_copy(0, 0, 0, 0, 0, 0).grid == 0                 # nothing to do
+    assert tp.workgroup_copy_workspace_bytes(0) == 0
+    with pytest.raises(ValueError):
+        tp.workgroup_copy_workspace_bytes(-1)
+
+
+def test_workgroup_copy_plan_errors():
+    n = 1000
+    need = tp.workgroup_copy_workspace_bytes(n)
+    W, S = 0x7f8000000000, 0x7fc000000000
+    f = tp.plan_workgroup_copy
+    assert _status(f, A, B, n, W, need - 1, S) == 1          # short workspace
+    assert _status(f, A, B, n, 0, need, S) == 1              # no workspace
+    assert _status(f, A, B, n, W, need, 0) == 1              # no status word
+    assert _status(f, A, B, -1, W, need, S) == 1
+    assert _status(f, A, B, (1 << 26) + 1, W, 1 << 40, S) == 1
+    assert _status(f, A, B, n, W, need, S, -1) == 1          # spin limit
+    assert _status(f, A, B, n, W, need, S, (1 << 24) + 1) == 1
+    assert _status(f, A + 2, B, n, W, need, S) == 2
+    assert _status(f, A, B, n, W + 2, need, S) == 2
+    assert _status(f, A, B, n, W, need, S + 2) == 2
+    assert _status(f, A, A + 256, n, W, need, S) == 4        # dst overlapping src in part
+    assert _status(f, A, B, n, B + 256, need, S) == 4        # workspace inside dst
+    assert _status(f, A, B, n, W, need, A + 8) == 4          # status inside src
+    assert _status(f, A, B, n, W, need, W + need - 4) == 4   # status inside the workspace

@@ -83,7 +83,8 @@ def kernels(disassembly):
 
 def test_kernels_present(kernels):
     names = " ".join(kernels)
-    for k in ("map_kernel", "chunk_copy_kernel", "row_shift_kernel"):
+    for k in ("map_kernel", "chunk_copy_kernel", "row_shift_kernel", "workgroup_copy_kernel",
+              "workgroup_copy_clear_kernel"):
         assert k in names
 
 
