@@ -344,6 +344,22 @@ TP_API int tp_workgroup_copy(const void *src, void *dst, int64_t n_chunks, void 
 TP_API int64_t tp_workgroup_copy_workspace_bytes(int64_t n_chunks);
 
 /*
+ * tp_workgroup_copy without a workspace argument and without allocating, for
+ * callers that cannot allocate (code under HIP graph capture, serving loops,
+ * harnesses that forbid hipMalloc). The flags and staging slots live in a
+ * static device array of 4 259 840 bytes that the library holds on each GPU
+ * it runs on, for up to 16384 chunks; n_chunks above that is
+ * TP_ERR_INVALID_ARG. The array is found once per device with
+ * hipGetSymbolAddress (with that device current) and never allocated or freed.
+ * Every call on one GPU shares that GPU's array and clears its flags first:
+ * calls that overlap in time on one GPU (other streams, other host threads)
+ * race and may give wrong results. src, dst, status, spin_limit, results and
+ * the other errors are those of tp_workgroup_copy.
+ */
+TP_API int tp_workgroup_copy_noalloc(const void *src, void *dst, int64_t n_chunks,
+                                     int32_t *status, int spin_limit, void *stream);
+
+/*
  * Host-only planning: the same validation and launch plan as the entry point
  * of the same name, for the given pointer values and LDS budget (bytes per
  * workgroup), without touching any device. Pointers are only inspected for

@@ -8,12 +8,13 @@ been built; there is no CPU fallback.
 from .tilepipe import (  # noqa: F401
     Align, TilepipeError, Path, Plan, Schedule, chunk_copy, device_check, lds_budget, library_path,
     map_2d, pipelined_map, plan_chunk_copy, plan_map, plan_map_2d, plan_row_shift,
-    plan_workgroup_copy, row_shift, workgroup_copy, workgroup_copy_workspace_bytes,
+    plan_workgroup_copy, row_shift, workgroup_copy, workgroup_copy_noalloc,
+    workgroup_copy_workspace_bytes,
 )
 
 __all__ = [
     "Align", "TilepipeError", "Path", "Plan", "Schedule", "chunk_copy", "device_check", "lds_budget",
     "library_path", "map_2d", "pipelined_map", "plan_chunk_copy", "plan_map", "plan_map_2d",
     "plan_row_shift", "plan_workgroup_copy", "row_shift", "workgroup_copy",
-    "workgroup_copy_workspace_bytes",
+    "workgroup_copy_noalloc", "workgroup_copy_workspace_bytes",
 ]

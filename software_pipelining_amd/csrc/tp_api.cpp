@@ -340,4 +340,45 @@ TP_API int tp_workgroup_copy(const void *src, void *dst, int64_t n_chunks, void 
     return finish_launch(tp::launch_workgroup_copy(plan, p, stream));
 }
 
+TP_API int tp_workgroup_copy_noalloc(const void *src, void *dst, int64_t n_chunks,
+                                     int32_t *status, int spin_limit, void *stream)
+{
+    if (n_chunks < 0 || n_chunks > tp::kWgNoAllocMaxChunks)
+        return TP_ERR_INVALID_ARG;
+    if (n_chunks == 0)
+        return tp::plan_workgroup_copy((uintptr_t)src, (uintptr_t)dst, 0, 0, 0,
+                                       (uintptr_t)status, spin_limit, nullptr);
+    // argument errors first, with a stand-in address that overlaps nothing
+    int st = tp::plan_workgroup_copy((uintptr_t)src, (uintptr_t)dst, n_chunks, 256,
+                                     tp::kWgNoAllocScratchBytes, (uintptr_t)status, spin_limit,
+                                     nullptr);
+    if (st == TP_ERR_OVERLAP)
+        st = TP_OK;   // decided again below, against the real address
+    if (st != TP_OK)
+        return st;
+    int64_t lds = 0;
+    if ((st = current_device(&lds)) != TP_OK)
+        return st;
+    void *ws = nullptr;
+    const int e = tp::workgroup_copy_scratch(&ws);
+    if (e != 0)
+        return hip_failure((hipError_t)e);
+    tp_plan plan;
+    st = tp::plan_workgroup_copy((uintptr_t)src, (uintptr_t)dst, n_chunks, (uintptr_t)ws,
+                                 tp::kWgNoAllocScratchBytes, (uintptr_t)status, spin_limit, &plan);
+    if (st != TP_OK)
+        return st;
+    if (plan.lds_bytes > lds)
+        return TP_ERR_LDS_BUDGET;
+    tp::WgCopyParams p{};
+    p.src = static_cast<const uint8_t *>(src);
+    p.dst = static_cast<uint8_t *>(dst);
+    p.flags = static_cast<uint32_t *>(ws);
+    p.stage = static_cast<uint8_t *>(ws) + tp::wg_stage_offset(n_chunks);
+    p.status = status;
+    p.n_chunks = n_chunks;
+    p.spin_limit = spin_limit == 0 ? tp::kWgDefaultSpinLimit : (uint32_t)spin_limit;
+    return finish_launch(tp::launch_workgroup_copy(plan, p, stream));
+}
+
 }  // extern "C"

@@ -199,6 +199,11 @@ constexpr int64_t kWgClearThreads = 256;       // lanes of a workgroup of the cl
 TP_HD constexpr int64_t wg_stage_offset(int64_t n) { return (4 * n + 255) / 256 * 256; }
 TP_HD constexpr int64_t wg_workspace_bytes(int64_t n) { return n <= 0 ? 0 : wg_stage_offset(n) + kWgChunkBytes * n; }
 
+// The allocation-free variant keeps its workspace in a static device array
+// sized for this many chunks.
+constexpr int64_t kWgNoAllocMaxChunks = 16384;
+constexpr int64_t kWgNoAllocScratchBytes = wg_workspace_bytes(kWgNoAllocMaxChunks);
+
 struct WgCopyParams {
     const uint8_t *src;
     uint8_t *dst;
@@ -283,5 +288,8 @@ int launch_chunk_copy(const tp_plan &plan, const ChunkParams &p, void *stream);
 // The clearing kernel (flags and status to zero), then, for two chunks or
 // more, the hand-off kernel.
 int launch_workgroup_copy(const tp_plan &plan, const WgCopyParams &p, void *stream);
+// Device address of the current device's static workspace for the
+// allocation-free variant (looked up once per device); a hipError_t value.
+int workgroup_copy_scratch(void **ptr);
 
 }  // namespace tp

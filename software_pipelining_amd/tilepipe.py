@@ -140,6 +140,7 @@ def _load():
         "tp_workgroup_copy": ([vp, vp, i64, vp, i64, vp, i32, vp], i32),
         "tp_workgroup_copy_workspace_bytes": ([i64], i64),
         "tp_plan_workgroup_copy": ([vp, vp, i64, vp, i64, vp, i32, pp], i32),
+        "tp_workgroup_copy_noalloc": ([vp, vp, i64, vp, i32, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -354,6 +355,26 @@ def workgroup_copy(src, dst, workspace=None, status=None, spin_limit: int = 0, s
                                        ctypes.c_void_p(status.data_ptr()), spin_limit,
                                        _stream_handle(src, stream))
     _check(st, "tp_workgroup_copy")
+    return status
+
+
+def workgroup_copy_noalloc(src, dst, status, spin_limit: int = 0, stream=None):
+    """workgroup_copy with the library's static per-device workspace (at most
+    16384 chunks; calls overlapping on one GPU race). status: int32 GPU
+    tensor of one element, written by the call."""
+    import torch
+    _require(src, torch.uint8, "src")
+    _require(dst, torch.uint8, "dst")
+    _require(status, torch.int32, "status")
+    if src.numel() != dst.numel() or src.numel() % 256:
+        raise ValueError("src and dst must hold the same whole number of 256-byte chunks")
+    _same_device(src, dst, status)
+    with torch.cuda.device(src.device):
+        st = _load().tp_workgroup_copy_noalloc(ctypes.c_void_p(src.data_ptr()),
+                                               ctypes.c_void_p(dst.data_ptr()), src.numel() // 256,
+                                               ctypes.c_void_p(status.data_ptr()), spin_limit,
+                                               _stream_handle(src, stream))
+    _check(st, "tp_workgroup_copy_noalloc")
     return status
 
 
