@@ -42,7 +42,8 @@ def parse():
                     help="consecutive tiles per workgroup (0: the library default)")
     ap.add_argument("--quick", action="store_true", help="headline only: no sweep, no extra rows")
     ap.add_argument("--mode", choices=("bench", "stages", "sweep", "occupancy", "map2d", "align",
-                                       "strides", "chunk", "misaligned"),
+                                       "strides", "chunk", "misaligned", "map2d_boxes",
+                                       "box_strides"),
                     default="bench",
                     help="stages: only the maps at 1-4 stages; sweep: only the 36-point stage/tile "
                          "sweep (both for hardware-counter passes); occupancy: scale2 bandwidth "
@@ -53,9 +54,11 @@ def parse():
                          "run width; chunk: only the chunk copy (the points of "
                          "CHUNK_COUNTER_POINTS, in order) and the runtime's 1 GiB copy, for "
                          "counter passes; misaligned: scale2 with the source on or 4 bytes off "
-                         "a line against the run length (MISALIGNED_POINTS)")
+                         "a line against the run length (MISALIGNED_POINTS); map2d_boxes: the "
+                         "2-D map with each box of MAP2D_BOXES in order, for counter passes; "
+                         "box_strides: those boxes at each row-stride pair of BOX_STRIDE_PAIRS")
     ap.add_argument("--rounds", type=int, default=1,
-                    help="interleaved rounds of --mode misaligned")
+                    help="interleaved rounds of --mode misaligned and --mode box_strides")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU work: read the rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE outputs "
@@ -439,6 +442,62 @@ def map2d_mode(args):
     torch.cuda.synchronize()
 
 
+def map2d_boxes_mode(args):
+    """The 2-D map workload (16384 x 16384 window, row stride 16448) with each
+    box of MAP2D_BOXES, `steps` launches each after one untimed, in that order
+    (a counter pass tells the boxes apart by dispatch order), then the
+    runtime's 1 GiB copy three times (the traffic counters' calibration)."""
+    import torch
+    import software_pipelining_amd as tp
+    dev = torch.device("cuda:0")
+    R, C, SS = MAP2D_ROWS, MAP2D_COLS, MAP2D_SRC_STRIDE
+    src = torch.empty(R, SS, device=dev).uniform_(-1, 1)[:, :C]
+    dst = torch.empty(R, C, device=dev)
+    flat = torch.empty(1 << 28, device=dev)
+    out = torch.empty_like(flat)
+    gpu_warmup(lambda: out.copy_(flat))          # clocks up, no map dispatch
+    for br, bc in MAP2D_BOXES:
+        f = lambda: tp.map_2d(src, dst, "scale2", br, bc, 2, 0)
+        per, _ = time_launches(f, 1, args.steps)
+        log(f"map_2d box {br}x{bc}: {median(per) * 1e3:.1f} us, "
+            f"{8 * R * C / (median(per) * 1e-3) / 1e9:.0f} GB/s")
+    for _ in range(3):
+        out.copy_(flat)
+    torch.cuda.synchronize()
+
+
+# (source row stride, destination row stride) pairs of the box-shape comparison,
+# in floats: the 2-D workload's own pair first, then both dense, each side alone
+# at 64 KiB + 256 B, and both at 64 KiB + 1 KiB.
+BOX_STRIDE_PAIRS = [(16448, 16384), (16384, 16384), (16384, 16448), (16448, 16448), (16640, 16640)]
+
+
+def box_strides_mode(args):
+    """scale2 over a 16384 x 16384 window with each box of MAP2D_BOXES (2 stages,
+    the library's run), for each row-stride pair of BOX_STRIDE_PAIRS, in
+    `rounds` interleaved rounds of `steps` launches; median microseconds."""
+    import torch
+    import software_pipelining_amd as tp
+    dev = torch.device("cuda:0")
+    R = C = 16384
+    src = {ss: torch.empty(R, ss, device=dev).uniform_(-1, 1)[:, :C]
+           for ss in sorted({ss for ss, _ in BOX_STRIDE_PAIRS})}
+    gpu_warmup(lambda: tp.map_2d(src[16384], src[16448], "scale2", 1, 1024, 2, 0))
+    res = {}
+    for _ in range(args.rounds):
+        for ss, ds in BOX_STRIDE_PAIRS:
+            dst = torch.empty(R, ds, device=dev)[:, :C]
+            for br, bc in MAP2D_BOXES:
+                f = lambda: tp.map_2d(src[ss], dst, "scale2", br, bc, 2, 0)
+                per, _ = time_launches(f, 1, args.steps)
+                res.setdefault((ss, ds, br, bc), []).append(median(per) * 1e3)
+            del dst
+    for ss, ds in BOX_STRIDE_PAIRS:
+        log(f"box strides src {ss} dst {ds}: " + "  ".join(
+            f"{br}x{bc} {median(res[(ss, ds, br, bc)]):.0f} us" for br, bc in MAP2D_BOXES))
+    torch.cuda.synchronize()
+
+
 def occupancy_mode(args):
     """scale2 over 2^28 at tiles 256/1024/4096, runs of 2/4/8, 1/2/4 stages:
     bandwidth with no bound on resident workgroups, with the library's bound,
@@ -809,6 +868,12 @@ def main():
         return
     if args.mode == "misaligned":
         misaligned_mode(args)
+        return
+    if args.mode == "map2d_boxes":
+        map2d_boxes_mode(args)
+        return
+    if args.mode == "box_strides":
+        box_strides_mode(args)
         return
 
     import numpy as np

@@ -44,14 +44,28 @@ def _run(cmd):
         raise RuntimeError("emulator build failed: " + " ".join(cmd) + "\n" + r.stderr[-4000:])
 
 
+def _fresh() -> bool:
+    return (os.path.exists(LIB) and
+            os.path.getmtime(LIB) >= max(os.path.getmtime(s) for s in _sources()))
+
+
 def build(force: bool = False) -> str:
     """Compile the emulator (host code only, the compilations in parallel) and
-    link it with the library's planner."""
-    if (not force and os.path.exists(LIB) and
-            os.path.getmtime(LIB) >= max(os.path.getmtime(s) for s in _sources())):
+    link it with the library's planner. Test processes running side by side
+    (pytest -n) take a file lock, so one builds and the others reuse it."""
+    if not force and _fresh():
         return LIB
-    from concurrent.futures import ThreadPoolExecutor
+    import fcntl
     os.makedirs(OUT, exist_ok=True)
+    with open(os.path.join(OUT, ".build.lock"), "w") as lock:
+        fcntl.flock(lock, fcntl.LOCK_EX)
+        if not force and _fresh():
+            return LIB
+        return _build_locked()
+
+
+def _build_locked() -> str:
+    from concurrent.futures import ThreadPoolExecutor
     inc = [f"-I{INCLUDE}", f"-I{CSRC}"]
     cmds, objs = [], []
     for src, part in UNITS:
