@@ -67,13 +67,19 @@ TP_HD __forceinline__ void pipeline_run(const E &e, int cnt, uint32_t ring, uint
                 consume(T, (T % S) * slot_bytes);
             }
         });
-        uint32_t cur = (S - 1) % S;  // slot of tile t
+        // Byte offsets of the slots of tiles t and t - 1, carried from one
+        // iteration to the next; tile t + S - 1 goes into tile t - 1's slot.
+        // Kept as offsets (adds and a wrap, no multiply) so that they stay
+        // scalar and M0 is set straight from them.
+        uint32_t cur = ((S - 1) % S) * slot_bytes;
+        uint32_t prev = ((2 * S - 2) % S) * slot_bytes;
+        const uint32_t ring_bytes = S * slot_bytes;
         for (int t = S - 1; t < cnt; ++t) {
-            const uint32_t nxt = cur == 0 ? S - 1 : cur - 1;  // slot of tile t + S - 1
-            issue(t + S - 1, ring + nxt * slot_bytes);
+            issue(t + S - 1, ring + prev);
             e.template wait<stage_wait_count(S, LD, ST, S - 1, true)>();
-            consume(t, cur * slot_bytes);
-            cur = cur + 1 == S ? 0 : cur + 1;
+            consume(t, cur);
+            prev = cur;
+            cur = cur + slot_bytes == ring_bytes ? 0 : cur + slot_bytes;
         }
     } else if constexpr (S == 1) {
         for (int t = 0; t < cnt; ++t) {
@@ -93,14 +99,16 @@ TP_HD __forceinline__ void pipeline_run(const E &e, int cnt, uint32_t ring, uint
                 consume(T, (T % S) * slot_bytes);
             }
         });
-        uint32_t cur = (S - 1) % S;  // slot of tile t
+        uint32_t cur = ((S - 1) % S) * slot_bytes;        // as above
+        uint32_t prev = ((2 * S - 2) % S) * slot_bytes;
+        const uint32_t ring_bytes = S * slot_bytes;
         for (int t = S - 1; t < cnt; ++t) {
-            const uint32_t nxt = cur == 0 ? S - 1 : cur - 1;  // slot of tile t + S - 1
             e.template wait<stage_wait_count(S, LD, ST, S - 1)>();
             e.barrier();
-            issue(t + S - 1, ring + nxt * slot_bytes);
-            consume(t, cur * slot_bytes);
-            cur = cur + 1 == S ? 0 : cur + 1;
+            issue(t + S - 1, ring + prev);
+            consume(t, cur);
+            prev = cur;
+            cur = cur + slot_bytes == ring_bytes ? 0 : cur + slot_bytes;
         }
     }
     // Operations retire in issue order and every path above ends with one
