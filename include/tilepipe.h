@@ -310,48 +310,51 @@ TP_API int tp_chunk_copy_ex(const void *src, void *dst, int64_t n_chunks, int ch
  *     dst[k] = src[k - 1]   (256 bytes each),  1 <= k < n_chunks;
  * chunk 0 of dst receives nothing and is not written. CDNA4 workgroups cannot
  * address each other's LDS, so the chunk passes through a staging slot in
- * `workspace`. The sender writes the slot at device scope (coherent across
- * the XCDs' L2s), waits for those stores, then sets a flag; the receiver polls
- * the flag and copies the slot into its LDS with device-scope loads before
- * storing it. A workgroup waits only for the one numbered just below it,
- * which was dispatched before it.
+ * `workspace`: each 4-byte word of it is stored together with a 4-byte tag in
+ * one 8-byte device-scope store (coherent across the XCDs' L2s), which lands
+ * as a whole. The receiver loads the slot the same way until every word's tag
+ * is set, so the arrival of the bytes is read off the bytes themselves; it
+ * puts them into its LDS and stores them. A workgroup waits only for the one
+ * numbered just below it, which was dispatched before it, and a sender waits
+ * for nothing but its own source load.
  *   src, dst: device buffers of n_chunks x 256 bytes, 4-byte aligned; dst ==
  *     src is allowed (each workgroup reads its own chunk before its receiver
  *     role writes it); a partial overlap is TP_ERR_OVERLAP.
  *   workspace: caller-owned device memory of at least
- *     tp_workgroup_copy_workspace_bytes(n_chunks) bytes, 4-byte aligned:
- *     n_chunks flag words, then 256-byte staging slots. The call clears the
- *     flags itself (a kernel on `stream` before the hand-off), so the
- *     workspace needs no preparation. Calls that share a workspace must not
+ *     tp_workgroup_copy_workspace_bytes(n_chunks) bytes (512 per chunk), 8-byte
+ *     aligned. The call zeroes the slots itself (a kernel on `stream` before
+ *     the hand-off), so the workspace needs no preparation and may be used
+ *     for anything else between calls. Calls that share a workspace must not
  *     overlap in time.
  *   status: caller-owned device int32. The call sets it to 0 and a receiver
  *     that gives up waiting sets it to 1; read it after the stream has
  *     finished. 1 means some dst chunks were not written.
- *   spin_limit: polls of its sender's flag before a receiver gives up
- *     (0 = the default of 65536; at most 2^24). A receiver that finds the
- *     status set stops polling too, so the kernel always finishes.
+ *   spin_limit: polls of its sender's slot before a receiver gives up
+ *     (0 = the default of 65536; at most 2^24). A waiting receiver also reads
+ *     the status every 8 polls and stops once it is set, so the kernel always
+ *     finishes.
  * n_chunks 0: TP_OK, nothing launched. More than 2^26 chunks, a missing
- * pointer or a short workspace: TP_ERR_INVALID_ARG; pointers not 4-byte
- * aligned: TP_ERR_MISALIGNED; workspace or status overlapping src or dst, or
- * each other: TP_ERR_OVERLAP.
+ * pointer or a short workspace: TP_ERR_INVALID_ARG; src, dst or status not
+ * 4-byte aligned, or the workspace not 8-byte aligned: TP_ERR_MISALIGNED;
+ * workspace or status overlapping src or dst, or each other: TP_ERR_OVERLAP.
  */
 TP_API int tp_workgroup_copy(const void *src, void *dst, int64_t n_chunks, void *workspace,
                              int64_t workspace_bytes, int32_t *status, int spin_limit,
                              void *stream);
 
-/* Bytes of workspace tp_workgroup_copy needs for n_chunks chunks (-1 if
- * n_chunks is out of range). */
+/* Bytes of workspace tp_workgroup_copy needs for n_chunks chunks, 512 per
+ * chunk (-1 if n_chunks is out of range). */
 TP_API int64_t tp_workgroup_copy_workspace_bytes(int64_t n_chunks);
 
 /*
  * tp_workgroup_copy without a workspace argument and without allocating, for
  * callers that cannot allocate (code under HIP graph capture, serving loops,
- * harnesses that forbid hipMalloc). The flags and staging slots live in a
- * static device array of 4 259 840 bytes that the library holds on each GPU
- * it runs on, for up to 16384 chunks; n_chunks above that is
- * TP_ERR_INVALID_ARG. The array is found once per device with
- * hipGetSymbolAddress (with that device current) and never allocated or freed.
- * Every call on one GPU shares that GPU's array and clears its flags first:
+ * harnesses that forbid hipMalloc). The staging slots live in a static
+ * device array of 8 388 608 bytes that the library holds on each GPU it runs
+ * on, for up to 16384 chunks; n_chunks above that is TP_ERR_INVALID_ARG. The
+ * array is found once per device with hipGetSymbolAddress (with that device
+ * current) and never allocated or freed.
+ * Every call on one GPU shares that GPU's array and zeroes its slots first:
  * calls that overlap in time on one GPU (other streams, other host threads)
  * race and may give wrong results. src, dst, status, spin_limit, results and
  * the other errors are those of tp_workgroup_copy.

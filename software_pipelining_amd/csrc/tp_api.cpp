@@ -332,8 +332,7 @@ TP_API int tp_workgroup_copy(const void *src, void *dst, int64_t n_chunks, void 
     tp::WgCopyParams p{};
     p.src = static_cast<const uint8_t *>(src);
     p.dst = static_cast<uint8_t *>(dst);
-    p.flags = static_cast<uint32_t *>(workspace);
-    p.stage = static_cast<uint8_t *>(workspace) + tp::wg_stage_offset(n_chunks);
+    p.stage = static_cast<uint8_t *>(workspace);
     p.status = status;
     p.n_chunks = n_chunks;
     p.spin_limit = spin_limit == 0 ? tp::kWgDefaultSpinLimit : (uint32_t)spin_limit;
@@ -373,8 +372,7 @@ TP_API int tp_workgroup_copy_noalloc(const void *src, void *dst, int64_t n_chunk
     tp::WgCopyParams p{};
     p.src = static_cast<const uint8_t *>(src);
     p.dst = static_cast<uint8_t *>(dst);
-    p.flags = static_cast<uint32_t *>(ws);
-    p.stage = static_cast<uint8_t *>(ws) + tp::wg_stage_offset(n_chunks);
+    p.stage = static_cast<uint8_t *>(ws);
     p.status = status;
     p.n_chunks = n_chunks;
     p.spin_limit = spin_limit == 0 ? tp::kWgDefaultSpinLimit : (uint32_t)spin_limit;

@@ -168,25 +168,14 @@ __device__ __forceinline__ void store_b32(const BufferRes &r, uint32_t voff, uin
 // one another. Device-scope loads and stores are what the compiler itself
 // emits for relaxed atomic loads and stores at device ("agent") scope on
 // gfx950, with no L2 write-back or invalidate: they are coherent across XCDs
-// on their own. Their order comes from the waits: a sender's data stores have
-// all completed (vmcnt 0) before it stores the flag, and a receiver issues its
-// data loads only after the flag load has returned. The compiler's release
-// and acquire sequences add an L2 write-back (buffer_wbl2) and invalidate
-// (buffer_inv) for ordinary stores and loads around the flag; those act on the
-// whole L2 of an XCD, and with one hand-off per workgroup they took 19 ms for
-// 2^20 chunks, against the device-scope data accesses used here.
-
-// A 4-byte LDS-DMA load at device scope (sc1): lane l's word lands at
-// m0 + 4 * l.
-__device__ __forceinline__ void dma_b32_device(const BufferRes &r, uint32_t voff, uint32_t m0)
-{
-    asm volatile("s_mov_b32 m0, %2\n\t"
-                 "s_nop 4\n\t"
-                 "buffer_load_dword %0, %1, 0 offen sc1 lds"
-                 :
-                 : "v"(voff), "s"(sgpr_res(r)), "s"(m0)
-                 : "memory");
-}
+// on their own. The compiler implements relaxed 64-bit atomics the same way,
+// with one 8-byte access (dwordx2): an aligned 8-byte device-scope store
+// becomes visible as a whole. So a 4-byte data word stored together with a
+// 4-byte tag in one such access needs no flag and no fence: a receiver whose
+// 8-byte load finds the tag has the data that came with it. (The compiler's
+// release and acquire sequences would add an L2 write-back (buffer_wbl2) and
+// invalidate (buffer_inv) that act on the whole L2 of an XCD; a flag protocol
+// built on them took 19 ms for 2^20 hand-offs.)
 
 // A 4-byte load at device scope into a register, complete when this returns
 // (the wait is part of the block, so the compiler sees the value only then).
@@ -202,11 +191,34 @@ __device__ __forceinline__ uint32_t load_b32_device(const BufferRes &r, uint32_t
     return v;
 }
 
-// A 4-byte store at device scope (a flag or status word).
+// An 8-byte load at device scope, one access, complete when this returns.
+__device__ __forceinline__ uint64_t load_b64_device(const BufferRes &r, uint32_t voff)
+{
+    uint64_t v;
+    asm volatile("s_nop 4\n\t"
+                 "buffer_load_dwordx2 %0, %1, %2, 0 offen sc1\n\t"
+                 "s_waitcnt vmcnt(0)"
+                 : "=v"(v)
+                 : "v"(voff), "s"(sgpr_res(r))
+                 : "memory");
+    return v;
+}
+
+// A 4-byte store at device scope (a header or status word).
 __device__ __forceinline__ void store_b32_device(const BufferRes &r, uint32_t voff, uint32_t v)
 {
     asm volatile("s_nop 4\n\t"
                  "buffer_store_dword %0, %1, %2, 0 offen sc1"
+                 :
+                 : "v"(v), "v"(voff), "s"(sgpr_res(r))
+                 : "memory");
+}
+
+// An 8-byte store at device scope, one access (a tagged word).
+__device__ __forceinline__ void store_b64_device(const BufferRes &r, uint32_t voff, uint64_t v)
+{
+    asm volatile("s_nop 4\n\t"
+                 "buffer_store_dwordx2 %0, %1, %2, 0 offen sc1"
                  :
                  : "v"(v), "v"(voff), "s"(sgpr_res(r))
                  : "memory");
@@ -288,19 +300,28 @@ struct GpuEngine {
         vm_wait<K>();
     }
     __device__ __forceinline__ void barrier() const { block_sync(); }
-    __device__ __forceinline__ void dma_b32_device(const BufferRes &r, uint32_t voff, uint32_t m0) const
-    {
-        dev::dma_b32_device(r, voff, m0);
-    }
     __device__ __forceinline__ uint32_t load_b32_device(const BufferRes &r, uint32_t voff) const
     {
         return dev::load_b32_device(r, voff);
+    }
+    __device__ __forceinline__ uint64_t load_b64_device(const BufferRes &r, uint32_t voff) const
+    {
+        return dev::load_b64_device(r, voff);
     }
     __device__ __forceinline__ void store_b32_device(const BufferRes &r, uint32_t voff, uint32_t v) const
     {
         dev::store_b32_device(r, voff, v);
     }
-    // a short pause between polls of a flag
+    __device__ __forceinline__ void store_b64_device(const BufferRes &r, uint32_t voff, uint64_t v) const
+    {
+        dev::store_b64_device(r, voff, v);
+    }
+    // true on every lane when p holds on every lane of the wave (a ballot)
+    __device__ __forceinline__ bool all_lanes(bool p) const
+    {
+        return __builtin_amdgcn_ballot_w64(!p) == 0;
+    }
+    // a short pause between polls
     __device__ __forceinline__ void pause() const { __builtin_amdgcn_s_sleep(1); }
 };
 

@@ -189,15 +189,29 @@ inline ChunkParams chunk_params(const tp_plan &plan, const void *src, void *dst,
 
 // ------------------------------------------------ copies between workgroups
 constexpr int kWgChunkBytes = 256;             // the chunk one workgroup hands on
+constexpr int kWgSlotBytes = 2 * kWgChunkBytes;   // its staging slot: 64 tagged 8-byte words
+constexpr uint32_t kWgTag = 1u;                // the tag of a word a sender has stored
 constexpr int64_t kWgMaxChunks = int64_t(1) << 26;
-constexpr uint32_t kWgDefaultSpinLimit = 1u << 16;   // polls of a flag before giving up
+constexpr uint32_t kWgDefaultSpinLimit = 1u << 16;   // polls of a slot before giving up
 constexpr uint32_t kWgMaxSpinLimit = 1u << 24;
+constexpr uint32_t kWgStatusPollEvery = 8;     // a waiting receiver reads the status every 8th poll
 constexpr int64_t kWgClearThreads = 256;       // lanes of a workgroup of the clearing kernel
+constexpr int64_t kWgClearSlotsPerPass = 8;    // slots (4 KiB) a clearing workgroup zeroes per pass
+constexpr int64_t kWgClearMaxGroups = 65536;   // the clearing kernel's grid at most (they loop)
 
-// Workspace of a copy between n workgroups: n flag words, then, from the next
-// 256-byte boundary, n staging slots of 256 bytes.
-TP_HD constexpr int64_t wg_stage_offset(int64_t n) { return (4 * n + 255) / 256 * 256; }
-TP_HD constexpr int64_t wg_workspace_bytes(int64_t n) { return n <= 0 ? 0 : wg_stage_offset(n) + kWgChunkBytes * n; }
+// Workspace of a copy between n workgroups: n staging slots of 512 bytes.
+// Slot k holds chunk k as 64 words {data, tag} of 8 bytes each, lane l's at
+// byte 8 l; the clearing kernel zeroes every slot, and a word is the sender's
+// once its tag reads kWgTag.
+TP_HD constexpr int64_t wg_workspace_bytes(int64_t n) { return n <= 0 ? 0 : kWgSlotBytes * n; }
+
+// Grid of the clearing kernel for n chunks.
+TP_HD constexpr int64_t wg_clear_groups(int64_t n)
+{
+    return (n + kWgClearSlotsPerPass - 1) / kWgClearSlotsPerPass < kWgClearMaxGroups
+               ? (n + kWgClearSlotsPerPass - 1) / kWgClearSlotsPerPass
+               : kWgClearMaxGroups;
+}
 
 // The allocation-free variant keeps its workspace in a static device array
 // sized for this many chunks.
@@ -207,11 +221,10 @@ constexpr int64_t kWgNoAllocScratchBytes = wg_workspace_bytes(kWgNoAllocMaxChunk
 struct WgCopyParams {
     const uint8_t *src;
     uint8_t *dst;
-    uint8_t *stage;          // n staging slots of kWgChunkBytes
-    uint32_t *flags;         // n words: flags[k] != 0 once chunk k is staged
+    uint8_t *stage;          // n staging slots of kWgSlotBytes
     int32_t *status;         // 0, or 1 once a receiver gave up waiting
     int64_t n_chunks;
-    uint32_t spin_limit;     // polls of a flag before a receiver gives up
+    uint32_t spin_limit;     // polls of a slot before a receiver gives up
     uint32_t pad;
 };
 
@@ -285,8 +298,8 @@ int launch_map2d_horner32_s5_8(const tp_plan &plan, const Map2dParams &p, void *
 int launch_map2d_copy_s1_4(const tp_plan &plan, const Map2dParams &p, void *stream);
 int launch_map2d_copy_s5_8(const tp_plan &plan, const Map2dParams &p, void *stream);
 int launch_chunk_copy(const tp_plan &plan, const ChunkParams &p, void *stream);
-// The clearing kernel (flags and status to zero), then, for two chunks or
-// more, the hand-off kernel.
+// The clearing kernel (staging slots and status to zero), then, for two
+// chunks or more, the hand-off kernel.
 int launch_workgroup_copy(const tp_plan &plan, const WgCopyParams &p, void *stream);
 // Device address of the current device's static workspace for the
 // allocation-free variant (looked up once per device); a hipError_t value.

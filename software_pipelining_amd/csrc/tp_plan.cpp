@@ -386,14 +386,15 @@ int plan_workgroup_copy(uintptr_t src, uintptr_t dst, int64_t n_chunks, uintptr_
     p.threads = 64;
     p.lane_chunks = 1;
     p.tiles_per_block = 1;
-    p.lds_bytes = 2 * kWgChunkBytes;
+    p.lds_bytes = 2 * kWgChunkBytes;   // the own chunk and the received one
     p.ring_bytes = p.lds_bytes;
     p.path = TP_PATH_SCALAR;
     if (n_chunks > 0) {
         const int64_t need = wg_workspace_bytes(n_chunks);
         if (!src || !dst || !workspace || !status || workspace_bytes < need)
             return TP_ERR_INVALID_ARG;
-        if (src % 4 || dst % 4 || workspace % 4 || status % 4)
+        // the tagged words are 8-byte accesses, which land whole only when aligned
+        if (src % 4 || dst % 4 || workspace % 8 || status % 4)
             return TP_ERR_MISALIGNED;
         const uint64_t bytes = (uint64_t)n_chunks * kWgChunkBytes;
         if (src != dst && overlaps(src, bytes, dst, bytes))

@@ -6,7 +6,7 @@
 
 namespace tp {
 
-// Workspace of tp_workgroup_copy_noalloc: flags and staging slots for at most
+// Workspace of tp_workgroup_copy_noalloc: the staging slots of at most
 // kWgNoAllocMaxChunks chunks. Each GPU the library runs on holds its own copy
 // until the process ends. In host code `scratch` names a host-side stand-in,
 // not the device array: only the address hipGetSymbolAddress returns for the
@@ -58,10 +58,9 @@ int launch_workgroup_copy(const tp_plan &plan, const WgCopyParams &p, void *stre
 {
     WgCopyParams args = p;
     void *kargs[] = {&args};
-    const int64_t clear_groups = (p.n_chunks + kWgClearThreads - 1) / kWgClearThreads;
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&dev::workgroup_copy_clear_kernel),
-                                   dim3((uint32_t)clear_groups), dim3((uint32_t)kWgClearThreads),
-                                   kargs, 0, (hipStream_t)stream);
+                                   dim3((uint32_t)wg_clear_groups(p.n_chunks)),
+                                   dim3((uint32_t)kWgClearThreads), kargs, 0, (hipStream_t)stream);
     if (e != hipSuccess || p.n_chunks < 2)
         return (int)e;
     e = hipLaunchKernel(reinterpret_cast<const void *>(&dev::workgroup_copy_kernel),

@@ -3,28 +3,28 @@
 //
 // The pages let one group of a cluster copy a chunk of its shared memory into
 // another group's shared memory; the receiver waits until the expected bytes
-// have arrived before it reads them, and both stay until the transfer is done
-// ("Asynchronous Copies", section "Copies between CTAs"). CDNA4 has no
-// clusters and no way to address another workgroup's LDS, so the chunk goes
-// through a staging slot in memory the two share:
+// have arrived before it reads them ("Asynchronous Copies", section "Copies
+// between CTAs"). CDNA4 has no clusters and no way to address another
+// workgroup's LDS, so the chunk goes through a staging slot in memory both
+// can reach, and "the bytes have arrived" is read off the bytes themselves:
+// every 4-byte word of the chunk travels with a 4-byte tag in one 8-byte
+// device-scope access, which lands whole (tp_engine.hpp), so a word whose tag
+// is set is the sender's word.
+//   clearing      zeroes every staging slot and the status word;
 //   workgroup k   copies chunk k of src into its LDS (LDS-DMA) and waits for
-//                 it; if k + 1 < n it stores the LDS bytes into staging slot
-//                 k at device scope, waits until those stores have completed
-//                 and sets flags[k] (a device-scope store);
-//   workgroup k   (k >= 1) polls flags[k - 1] at device scope; once it is set,
-//                 copies staging slot k - 1 into its LDS with device-scope
-//                 LDS-DMA loads, waits, and stores those bytes as chunk k of
-//                 dst.
-// (tp_engine.hpp explains why device-scope accesses and these waits order the
-// hand-off across XCDs.)
+//                 it; if k + 1 < n each lane stores its word with the tag into
+//                 staging slot k (no wait, no flag);
+//   workgroup k   (k >= 1) loads slot k - 1, one tagged word per lane, until
+//                 every lane's tag is set, puts the words into its LDS and
+//                 stores them as chunk k of dst.
 // A workgroup only ever waits for the one numbered just below it. Workgroups
 // are dispatched in order of their index, so the lowest one not yet finished
-// is running or has room to start, and the chain always moves. The wait is
-// still bounded: after spin_limit polls the receiver gives up, sets the status
-// word and writes nothing, and a receiver that sees the status set stops
-// waiting too, so every wave ends whatever happens. Each staging slot is used
-// once per call; the flags and the status start at zero (the clearing kernel
-// runs first on the same stream).
+// is running or has room to start, and the chain always moves; a sender
+// never waits for anything but its own source load. The wait is still
+// bounded: after spin_limit polls the receiver gives up, sets the status word
+// and writes nothing, and a receiver that finds the status set (it looks
+// every kWgStatusPollEvery polls) stops waiting too, so every wave ends
+// whatever happens.
 #pragma once
 
 #include "tp_engine.hpp"
@@ -33,17 +33,22 @@
 namespace tp {
 namespace dev {
 
-// Zero flags [0, n) and the status word: workgroups of kWgClearThreads lanes,
-// one flag word per lane.
+// Zero the n staging slots and the status word. Workgroups of kWgClearThreads
+// lanes zero kWgClearSlotsPerPass slots (4 KiB, 16 bytes a lane) per pass and
+// step over the slots by the grid.
 template <class E>
 TP_HD __forceinline__ void workgroup_copy_clear_body(const E &e, const WgCopyParams &p)
 {
+    constexpr int64_t kPassBytes = kWgClearSlotsPerPass * kWgSlotBytes;
+    static_assert(kPassBytes == kWgClearThreads * 16, "one 16-byte store per lane and pass");
     const uint32_t tid = e.tid();
-    const int64_t first = (int64_t)e.block() * kWgClearThreads;
-    const int64_t left = p.n_chunks - first;
-    const uint32_t count = (uint32_t)(left < kWgClearThreads ? left : kWgClearThreads);
-    const auto rflags = e.res(p.flags + first, count * 4);
-    e.store_b32(rflags, tid * 4, 0u);
+    const int64_t total = p.n_chunks * kWgSlotBytes;
+    for (int64_t at = (int64_t)e.block() * kPassBytes; at < total;
+         at += (int64_t)e.blocks() * kPassBytes) {
+        const int64_t left = total - at;
+        const auto rslots = e.res(p.stage + at, (uint32_t)(left < kPassBytes ? left : kPassBytes));
+        e.store_b128(rslots, tid * 16, u32x4{0u, 0u, 0u, 0u});
+    }
     if (e.block() == 0) {
         const auto rstatus = e.res(p.status, 4);
         e.store_b32(rstatus, tid == 0 ? 0u : 4u, 0u);
@@ -65,39 +70,36 @@ TP_HD __forceinline__ void workgroup_copy_body(const E &e, const WgCopyParams &p
     e.template wait<0>();
 
     if (k + 1 < p.n_chunks) {             // send chunk k to workgroup k + 1
-        const auto rstage = e.res(p.stage + kWgChunkBytes * k, kWgChunkBytes);
-        e.store_b32_device(rstage, off, e.template lds_load<uint32_t>(off));
-        e.template wait<0>();             // the staged bytes are written before the flag
-        const auto rflag = e.res(p.flags + k, 4);
-        e.store_b32_device(rflag, lane == 0 ? 0u : 4u, 1u);
+        const auto rslot = e.res(p.stage + kWgSlotBytes * k, kWgSlotBytes);
+        const uint64_t word = (uint64_t)kWgTag << 32 | e.template lds_load<uint32_t>(off);
+        e.store_b64_device(rslot, lane * 8, word);
     }
 
     if (k >= 1) {                         // receive chunk k - 1 from workgroup k - 1
-        const auto rflag = e.res(p.flags + (k - 1), 4);
+        const auto rslot = e.res(p.stage + kWgSlotBytes * (k - 1), kWgSlotBytes);
         const auto rstatus = e.res(p.status, 4);
-        uint32_t got = 0, stop = 0;
+        uint64_t word = 0;
+        bool got = false, stop = false;
         for (uint32_t i = 0; i < p.spin_limit; ++i) {
-            got = e.uniform(e.load_b32_device(rflag, 0));
+            word = e.load_b64_device(rslot, lane * 8);
+            got = e.all_lanes((uint32_t)(word >> 32) == kWgTag);
             if (got)
                 break;
-            stop = e.uniform(e.load_b32_device(rstatus, 0));
-            if (stop)
-                break;
+            if (i % kWgStatusPollEvery == kWgStatusPollEvery - 1) {
+                stop = e.uniform(e.load_b32_device(rstatus, 0)) != 0;
+                if (stop)
+                    break;
+            }
             e.pause();
         }
         if (got) {
-            const auto rstage = e.res(p.stage + kWgChunkBytes * (k - 1), kWgChunkBytes);
-            e.dma_b32_device(rstage, off, e.uniform(base + kWgChunkBytes));
-            e.template wait<0>();
+            e.template lds_store<uint32_t>(kWgChunkBytes + off, (uint32_t)word);
             const auto rdst = e.res(p.dst + kWgChunkBytes * k, kWgChunkBytes);
             e.store_b32(rdst, off, e.template lds_load<uint32_t>(kWgChunkBytes + off));
         } else if (!stop) {
-            const auto rstatus_w = e.res(p.status, 4);
-            e.store_b32_device(rstatus_w, lane == 0 ? 0u : 4u, 1u);   // gave up waiting
+            e.store_b32_device(rstatus, lane == 0 ? 0u : 4u, 1u);   // gave up waiting
         }
     }
-    // no copy into LDS is in flight when the workgroup ends
-    e.template wait<0>();
 }
 
 }  // namespace dev

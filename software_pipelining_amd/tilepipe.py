@@ -330,7 +330,8 @@ def workgroup_copy(src, dst, workspace=None, status=None, spin_limit: int = 0, s
     k - 1 of src, handed from workgroup k - 1 to workgroup k; dst chunk 0 is
     not written. src, dst: uint8 GPU tensors of the same whole number of
     256-byte chunks. workspace: uint8 GPU tensor of at least
-    workgroup_copy_workspace_bytes(n) bytes (allocated here when None).
+    workgroup_copy_workspace_bytes(n) bytes, 8-byte aligned (allocated here
+    when None).
     status: int32 GPU tensor of one element (allocated when None), 0 after the
     stream has run the call, 1 if some receiver gave up waiting. Returns the
     status tensor (reading it synchronizes)."""

@@ -98,23 +98,26 @@ struct Res {
 };
 
 enum Kind { K_NONE, K_UNIFORM, K_LDS_LOAD, K_DMA, K_STORE, K_WAIT, K_BARRIER, K_DONE, K_LDS_STORE,
-            K_LOAD };
+            K_LOAD, K_ALL };
 
 inline const char *kind_name(int k)
 {
     static const char *n[] = {"none", "readfirstlane", "LDS read", "LDS-DMA load", "store",
-                              "vmcnt wait", "barrier", "end", "LDS write", "register load"};
+                              "vmcnt wait", "barrier", "end", "LDS write", "register load",
+                              "ballot"};
     return n[k];
 }
 
 struct Request {
     int kind = K_NONE;
     uint32_t a = 0, b = 0;   // UNIFORM: a = value; LDS_LOAD, LDS_STORE: a = offset, b = size;
-                             // DMA: a = voff, b = m0; STORE, LOAD: a = voff; WAIT: a = K
-    int width = 0;           // DMA/STORE: 16, 4 or 1 bytes
+                             // DMA: a = voff, b = m0; STORE, LOAD: a = voff; WAIT: a = K;
+                             // ALL: a = the lane's predicate
+    int width = 0;           // DMA/STORE: 16, 8, 4 or 1 bytes; LOAD: 8 or 4
     Res res{};
     uint8_t data[16];        // STORE and LDS_STORE data, LDS_LOAD result
-    uint32_t result = 0;     // UNIFORM result
+    uint32_t result = 0;     // UNIFORM, ALL and 4-byte LOAD result
+    uint64_t wide = 0;       // 8-byte LOAD result
 };
 
 struct Lane {
@@ -308,6 +311,14 @@ class Emulator {
         case K_LDS_LOAD: lds_read(w); break;
         case K_LDS_STORE: lds_write(w); break;
         case K_LOAD: reg_load(w); break;
+        case K_ALL: {
+            uint32_t all = 1;
+            for (Lane *l : w.lanes)
+                all &= l->req.a != 0;
+            for (Lane *l : w.lanes)
+                l->req.result = all;
+            break;
+        }
         case K_DMA: dma(w); break;
         case K_STORE: store(w); break;
         case K_WAIT: {
@@ -494,17 +505,19 @@ class Emulator {
         for (Lane *l : w.lanes) {
             const Res &r = l->req.res;
             const uint64_t o = l->req.a;
-            uint32_t v = 0;
-            if (o + 4 <= r.num_records) {
+            const int width = l->req.width == 8 ? 8 : 4;
+            uint64_t v = 0;
+            if (o + width <= r.num_records) {
                 const uint64_t g = r.base + o;
-                if (!region_of(g, 4))
-                    fail("workgroup %u wave %d lane %u: load of 4 bytes at offset %llu of a "
+                if (!region_of(g, width))
+                    fail("workgroup %u wave %d lane %u: load of %d bytes at offset %llu of a "
                          "buffer at %#llx (num_records %u) reads outside every buffer of the "
-                         "call", block, w.id, l->tid, (unsigned long long)o,
+                         "call", block, w.id, l->tid, width, (unsigned long long)o,
                          (unsigned long long)r.base, r.num_records);
-                memcpy(&v, reinterpret_cast<const void *>(g), 4);
+                memcpy(&v, reinterpret_cast<const void *>(g), width);
             }
-            l->req.result = v;
+            l->req.result = (uint32_t)v;
+            l->req.wide = v;
         }
     }
 
@@ -623,18 +636,37 @@ struct EmuEngine {
         g_emu->post(q);
     }
     // Device-scope accesses: the emulator's memory is one coherent store, so
-    // they are the plain ones.
-    void dma_b32_device(const Res &r, uint32_t voff, uint32_t m0) const { dma(r, voff, m0, 4); }
+    // they are the plain ones, and an 8-byte store or load is one access.
     uint32_t load_b32_device(const Res &r, uint32_t voff) const
     {
         Request q;
         q.kind = K_LOAD;
         q.a = voff;
+        q.width = 4;
         q.res = r;
         g_emu->post(q);
         return g_lane->req.result;
     }
+    uint64_t load_b64_device(const Res &r, uint32_t voff) const
+    {
+        Request q;
+        q.kind = K_LOAD;
+        q.a = voff;
+        q.width = 8;
+        q.res = r;
+        g_emu->post(q);
+        return g_lane->req.wide;
+    }
     void store_b32_device(const Res &r, uint32_t voff, uint32_t v) const { store(r, voff, &v, 4); }
+    void store_b64_device(const Res &r, uint32_t voff, uint64_t v) const { store(r, voff, &v, 8); }
+    bool all_lanes(bool p) const
+    {
+        Request q;
+        q.kind = K_ALL;
+        q.a = p ? 1u : 0u;
+        g_emu->post(q);
+        return g_lane->req.result != 0;
+    }
     void pause() const {}
 };
 

@@ -99,14 +99,13 @@ int emu_workgroup_copy(const void *src, void *dst, int64_t n_chunks, void *works
     tp::WgCopyParams p{};
     p.src = static_cast<const uint8_t *>(src);
     p.dst = static_cast<uint8_t *>(dst);
-    p.flags = static_cast<uint32_t *>(workspace);
-    p.stage = static_cast<uint8_t *>(workspace) + tp::wg_stage_offset(n_chunks);
+    p.stage = static_cast<uint8_t *>(workspace);
     p.status = status;
     p.n_chunks = n_chunks;
     p.spin_limit = spin_limit == 0 ? tp::kWgDefaultSpinLimit : (uint32_t)spin_limit;
     tp_plan clear = plan;
     clear.threads = (int32_t)tp::kWgClearThreads;
-    clear.grid = (n_chunks + tp::kWgClearThreads - 1) / tp::kWgClearThreads;
+    clear.grid = tp::wg_clear_groups(n_chunks);
     clear.lds_bytes = 0;
     emu::Options co = *o;
     co.blocks = nullptr;

@@ -1,6 +1,6 @@
 """GPU parity of tp_workgroup_copy against the oracle (bit-exact), through the
 C ABI: chunk k of the source, loaded into workgroup k's LDS, is handed to
-workgroup k + 1 through a staging slot and a device-scope flag and written as
+workgroup k + 1 through a staging slot of tagged 8-byte words and written as
 chunk k + 1 of the destination ("Asynchronous Copies", section "Copies between
 CTAs"). Guard words around every buffer catch a write outside it. A tiny spin
 limit, set from the host, makes receivers give up early: every chunk must then
@@ -119,7 +119,8 @@ def test_graph_replays(cuda_device):
 
 
 def test_tiny_spin_limit_gives_up_cleanly(cuda_device):
-    # one poll per receiver: some receivers may find no flag yet and give up;
+    # one poll per receiver: some receivers may find their slot not yet
+    # tagged and give up;
     # every chunk is then either the received one or untouched, and the status
     # is 1 exactly when some chunk was not written
     n = 1 << 14
@@ -149,7 +150,7 @@ def test_errors(cuda_device):
     with pytest.raises(tp.TilepipeError) as e:
         tp.workgroup_copy(src, dst, short, status)
     assert e.value.status == 1
-    big = torch.zeros(2 * n * CHUNK, dtype=torch.uint8, device=cuda_device)
+    big = torch.zeros(4 * n * CHUNK, dtype=torch.uint8, device=cuda_device)
     with pytest.raises(tp.TilepipeError) as e:       # dst overlapping src in part
         tp.workgroup_copy(big[:n * CHUNK], big[CHUNK:(n + 1) * CHUNK])
     assert e.value.status == 4

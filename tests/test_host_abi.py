@@ -524,7 +524,7 @@ def test_header_is_plain_c():
 def test_workgroup_copy_plan():
     n = 1000
     need = tp.workgroup_copy_workspace_bytes(n)
-    assert need == (4 * n + 255) // 256 * 256 + 256 * n
+    assert need == 512 * n                  # 64 tagged 8-byte words per chunk
     W, S = 0x7f8000000000, 0x7fc000000000
     p = tp.plan_workgroup_copy(A, B, n, W, need, S)
     assert (p.grid, p.threads, p.lds_bytes, p.tile_units) == (n, 64, 512, 256)
@@ -549,6 +549,7 @@ def test_workgroup_copy_plan_errors():
     assert _status(f, A, B, n, W, need, S, (1 << 24) + 1) == 1
     assert _status(f, A + 2, B, n, W, need, S) == 2
     assert _status(f, A, B, n, W + 2, need, S) == 2
+    assert _status(f, A, B, n, W + 4, need, S) == 2          # tagged words need 8-byte alignment
     assert _status(f, A, B, n, W, need, S + 2) == 2
     assert _status(f, A, A + 256, n, W, need, S) == 4        # dst overlapping src in part
     assert _status(f, A, B, n, B + 256, need, S) == 4        # workspace inside dst

@@ -1,7 +1,7 @@
 """The allocation-free copy between workgroups (tp_workgroup_copy_noalloc,
 through the C ABI) against the entry point that takes a caller workspace
 (tp_workgroup_copy): bit-exact on two calls in a row, the second smaller, so
-the static workspace keeps the first call's flags and slots when the second
+the static workspace keeps the first call's tagged slots when the second
 runs. Both are also checked against the oracle."""
 import numpy as np
 import pytest
